@@ -1,0 +1,162 @@
+/*
+ * parallax.h - C ABI of libparallax, the MI355X (gfx950) Parallax forward pass.
+ *
+ * Parallax ("Parallax: Parameterized Local Linear Attention for Language
+ * Modeling", paper page, "Abstract"; explainer blog "Parallax: Breaking the
+ * Boundary Bias with Parameterized Local Linear Attention", section "The Core
+ * Insight: Covariance Correction", output equation) computes, for each query,
+ * softmax attention minus the key/value covariance applied to a learned
+ * per-head probe rho:
+ *
+ *     w_i   = softmax_i(scale * q . k_i)
+ *     mu_v  = sum_i w_i v_i,   mu_k = sum_i w_i k_i
+ *     S_KV  = sum_i w_i (v_i - mu_v)(k_i - mu_k)^T      (value rows, key columns)
+ *     out   = mu_v - S_KV rho
+ *
+ * The blog's "Hardware Efficiency" section describes a decode kernel that
+ * fuses the softmax and covariance branches into one pass over the KV stream;
+ * these entry points do that on CDNA4. Readings of points the pages leave
+ * open: rho is in key space and is not multiplied by `scale`; the covariance
+ * is centred at the softmax-weighted means and uses the softmax weights
+ * (summing to one); GQA groups are contiguous (query head h reads KV head
+ * h / (H_q / H_kv)); a query that sees no key outputs zeros.
+ *
+ * Conventions shared by every call:
+ *  - Tensor pointers are DEVICE pointers to dense row-major arrays (last
+ *    dimension contiguous) on the current HIP device; they must be 16-byte
+ *    aligned. The caller owns every buffer; the library never allocates or
+ *    frees memory, never synchronises, and keeps no mutable global state (a
+ *    lazily filled, thread-safe cache of per-device compute-unit counts is the
+ *    only global).
+ *  - Inputs are read only. `out` is written in full (every element).
+ *  - `dtype` is the storage type of q, rho, K and V (bf16 or fp32); all
+ *    accumulation is fp32 and `out` is always fp32.
+ *  - `seq_lens` is a device int32 array [B]. Its values cannot be checked on
+ *    the host without a synchronisation, so kernels clamp them to [0, S_max]
+ *    (for prefill, rows t >= seq_lens[b] are written as zeros). Keys at or past
+ *    a sequence's length are never read into the result (NaN padding there is
+ *    harmless).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL means the null
+ *    stream). Every argument check happens on the host before any launch: on
+ *    an error status nothing has been launched and no buffer was touched.
+ *    Launch failures return PARALLAX_ERR_HIP. No call throws.
+ *  - Supported: head dim d in {64, 128}; G = H_q / H_kv integral with
+ *    G <= 4 or G a multiple of 4 (groups of 4 query heads share one pass over
+ *    their KV head; larger G re-reads K/V once per group of 4); each (b, h_kv)
+ *    slice of K or V must be smaller than 2 GiB.
+ */
+#ifndef PARALLAX_H
+#define PARALLAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARALLAX_ABI_VERSION 1
+
+typedef enum {
+  PARALLAX_OK = 0,
+  PARALLAX_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  PARALLAX_ERR_BAD_SHAPE = 2,    /* a size <= 0, H_q % H_kv != 0, T > S_max, ... */
+  PARALLAX_ERR_UNSUPPORTED = 3,  /* d, G, dtype or size outside what is built */
+  PARALLAX_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
+  PARALLAX_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required */
+  PARALLAX_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} parallax_status_t;
+
+typedef enum { PARALLAX_BF16 = 0, PARALLAX_F32 = 1 } parallax_dtype_t;
+
+/* PARALLAX_ABI_VERSION of the built library. */
+int parallax_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* parallax_status_string(parallax_status_t s);
+
+/*
+ * Split-KV plan for decode. Each (b, KV head, group of <= 4 query heads) is
+ * cut into `num_splits` contiguous key ranges of `chunk` keys (a multiple of
+ * 128), processed by separate workgroups whose partial softmax states are
+ * merged by the combine step. `requested` = 0 picks a plan from the device's
+ * compute-unit count; a positive value asks for that many splits (rounded so
+ * that chunk is a multiple of 128). Writes the plan to *num_splits and *chunk
+ * (either may be NULL). Returns PARALLAX_ERR_BAD_SHAPE for sizes <= 0 or
+ * H_q % H_kv != 0, PARALLAX_ERR_HIP if the device cannot be queried.
+ */
+parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int S_max, int requested,
+                                       int* num_splits, int* chunk);
+
+/*
+ * Workspace bytes needed by parallax_decode / parallax_decode_partial for the
+ * plan `num_splits` (as returned by parallax_decode_plan): one fp32 record of
+ * (2 d + 4) values (running max, weight sum, probe sum, probe reference, and
+ * two d-vectors) per (b, h_q, split). 0 if num_splits == 1 (the partial kernel
+ * then finalises directly) or on a bad shape.
+ */
+size_t parallax_decode_workspace_size(int B, int H_q, int d, int num_splits);
+
+/*
+ * Decode: one new query per (b, h_q) against the first seq_lens[b] cached keys.
+ *   q, rho    [B, H_q, d]          dtype
+ *   k_cache   [B, H_kv, S_max, d]  dtype
+ *   v_cache   [B, H_kv, S_max, d]  dtype
+ *   seq_lens  [B]                  int32 (device)
+ *   out       [B, H_q, d]          fp32, written in full
+ *   scale     softmax scale applied to q . k only (never to rho . k)
+ *   num_splits 0 = automatic plan, else the requested split count
+ *   workspace  device scratch of at least parallax_decode_workspace_size()
+ *              bytes for the resolved plan (may be NULL when that is 0)
+ * Equivalent to parallax_decode_partial followed by parallax_decode_combine
+ * (a single launch when the plan has one split).
+ */
+parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_cache,
+                                  const void* v_cache, const int32_t* seq_lens, float* out,
+                                  int B, int H_q, int H_kv, int d, int S_max, float scale,
+                                  parallax_dtype_t dtype, int num_splits, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * First phase of decode: streams every valid K/V row once and writes one
+ * partial state per (b, h_q, split) to `workspace` (or, when the resolved
+ * plan has one split, finalises straight into `out`, which may otherwise be
+ * NULL). Arguments as parallax_decode.
+ */
+parallax_status_t parallax_decode_partial(const void* q, const void* rho, const void* k_cache,
+                                          const void* v_cache, const int32_t* seq_lens,
+                                          float* out, int B, int H_q, int H_kv, int d,
+                                          int S_max, float scale, parallax_dtype_t dtype,
+                                          int num_splits, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
+ * Second phase of decode: merges the partial states written by
+ * parallax_decode_partial with the same (B, H_q, H_kv, d, S_max, num_splits)
+ * and writes out [B, H_q, d] fp32. Splits that start at or past seq_lens[b]
+ * are skipped (never read). A no-op returning PARALLAX_OK when the resolved
+ * plan has one split.
+ */
+parallax_status_t parallax_decode_combine(const int32_t* seq_lens, float* out, int B, int H_q,
+                                          int H_kv, int d, int S_max, int num_splits,
+                                          const void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
+ * Causal prefill: query row t of sequence b sees keys 0..t (no past offset).
+ *   q, rho    [B, H_q, T, d]       dtype (rho is per token)
+ *   k, v      [B, H_kv, S_max, d]  dtype, T <= S_max
+ *   seq_lens  [B]                  int32 (device); rows t >= seq_lens[b] -> 0
+ *   out       [B, H_q, T, d]       fp32, written in full
+ * Needs no workspace. Only dtype PARALLAX_BF16 is built for prefill.
+ */
+parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k,
+                                   const void* v, const int32_t* seq_lens, float* out, int B,
+                                   int H_q, int H_kv, int d, int T, int S_max, float scale,
+                                   parallax_dtype_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H */

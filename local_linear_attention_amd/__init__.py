@@ -1,0 +1,226 @@
+"""Python binding of libparallax, the MI355X Parallax forward pass.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (``include/parallax.h``). PyTorch supplies device
+memory and the current stream. There is no CPU fallback: if the library is
+not built, every call raises.
+
+Functions mirror the C entry points:
+
+* ``decode_plan``, ``decode_workspace_size``
+* ``decode`` (one shot), ``decode_partial`` + ``decode_combine`` (two phases)
+* ``prefill`` (causal)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ParallaxError", "lib", "library_path", "abi_version", "status_string", "decode_plan",
+    "decode_workspace_size", "decode", "decode_partial", "decode_combine", "prefill",
+    "STATUS", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libparallax.so")
+
+STATUS = {
+    0: "PARALLAX_OK",
+    1: "PARALLAX_ERR_NULL_POINTER",
+    2: "PARALLAX_ERR_BAD_SHAPE",
+    3: "PARALLAX_ERR_UNSUPPORTED",
+    4: "PARALLAX_ERR_MISALIGNED",
+    5: "PARALLAX_ERR_WORKSPACE",
+    6: "PARALLAX_ERR_HIP",
+}
+_BF16, _F32 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "parallax_abi_version", "parallax_status_string", "parallax_decode_plan",
+    "parallax_decode_workspace_size", "parallax_decode", "parallax_decode_partial",
+    "parallax_decode_combine", "parallax_prefill",
+)
+
+
+class ParallaxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libparallax.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m local_linear_attention_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.parallax_abi_version.restype = i
+    L.parallax_abi_version.argtypes = []
+    L.parallax_status_string.restype = ctypes.c_char_p
+    L.parallax_status_string.argtypes = [i]
+    L.parallax_decode_plan.restype = i
+    L.parallax_decode_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.parallax_decode_workspace_size.restype = sz
+    L.parallax_decode_workspace_size.argtypes = [i, i, i, i]
+    dec = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.parallax_decode.restype = i
+    L.parallax_decode.argtypes = dec
+    L.parallax_decode_partial.restype = i
+    L.parallax_decode_partial.argtypes = dec
+    L.parallax_decode_combine.restype = i
+    L.parallax_decode_combine.argtypes = [vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    L.parallax_prefill.restype = i
+    L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().parallax_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().parallax_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise ParallaxError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev_tensor(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def decode_plan(B: int, H_q: int, H_kv: int, S_max: int, num_splits: int = 0):
+    """(num_splits, chunk) the library uses for these sizes (0 = automatic)."""
+    ns, ch = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().parallax_decode_plan(B, H_q, H_kv, S_max, num_splits, ctypes.byref(ns),
+                                      ctypes.byref(ch)), "parallax_decode_plan")
+    return ns.value, ch.value
+
+
+def decode_workspace_size(B: int, H_q: int, d: int, num_splits: int) -> int:
+    return int(lib().parallax_decode_workspace_size(B, H_q, d, num_splits))
+
+
+def _decode_shapes(q, rho, k_cache, v_cache, seq_lens):
+    for name, t in (("q", q), ("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("seq_lens", seq_lens)):
+        _dev_tensor(t, name)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q is [B, H_q, d] and k_cache is [B, H_kv, S_max, d]")
+    B, H_q, d = q.shape
+    _, H_kv, S_max, _ = k_cache.shape
+    if rho.shape != q.shape or v_cache.shape != k_cache.shape or k_cache.shape[0] != B \
+            or k_cache.shape[3] != d:
+        raise ValueError("inconsistent decode shapes")
+    if not (q.dtype == rho.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, rho, k_cache and v_cache must share one dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    return B, H_q, H_kv, d, S_max
+
+
+def _workspace(B, H_q, H_kv, d, S_max, num_splits, workspace, device):
+    ns, _ = decode_plan(B, H_q, H_kv, S_max, num_splits)
+    need = decode_workspace_size(B, H_q, d, ns)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 1, dtype=torch.float32, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def decode(q, rho, k_cache, v_cache, seq_lens, scale: float, *, num_splits: int = 0, out=None,
+           workspace=None):
+    """Parallax decode; returns out [B, H_q, d] fp32 (see parallax_decode)."""
+    B, H_q, H_kv, d, S_max = _decode_shapes(q, rho, k_cache, v_cache, seq_lens)
+    if out is None:
+        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    ws, ws_bytes = _workspace(B, H_q, H_kv, d, S_max, num_splits, workspace, q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_decode(
+            q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            seq_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, S_max, float(scale),
+            _dtype_code(q), int(num_splits), ws.data_ptr(), ws_bytes, _stream_ptr(q.device)),
+            "parallax_decode")
+    return out
+
+
+def decode_partial(q, rho, k_cache, v_cache, seq_lens, scale: float, workspace, *,
+                   num_splits: int = 0, out=None):
+    """First decode phase (partial states into ``workspace``; see parallax_decode_partial)."""
+    B, H_q, H_kv, d, S_max = _decode_shapes(q, rho, k_cache, v_cache, seq_lens)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_decode_partial(
+            q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            seq_lens.data_ptr(), 0 if out is None else out.data_ptr(), B, H_q, H_kv, d, S_max,
+            float(scale), _dtype_code(q), int(num_splits), workspace.data_ptr(), ws_bytes,
+            _stream_ptr(q.device)), "parallax_decode_partial")
+    return out
+
+
+def decode_combine(seq_lens, out, workspace, *, H_kv: int, S_max: int, num_splits: int = 0):
+    """Second decode phase: merges the workspace into ``out`` [B, H_q, d]."""
+    _dev_tensor(out, "out")
+    B, H_q, d = out.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(out.device):
+        _check(lib().parallax_decode_combine(
+            seq_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, S_max, int(num_splits),
+            workspace.data_ptr(), ws_bytes, _stream_ptr(out.device)), "parallax_decode_combine")
+    return out
+
+
+def prefill(q, rho, k, v, seq_lens, scale: float, *, out=None):
+    """Causal Parallax prefill; returns out [B, H_q, T, d] fp32 (see parallax_prefill)."""
+    for name, t in (("q", q), ("rho", rho), ("k", k), ("v", v), ("seq_lens", seq_lens)):
+        _dev_tensor(t, name)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q is [B, H_q, T, d] and k is [B, H_kv, S_max, d]")
+    B, H_q, T, d = q.shape
+    _, H_kv, S_max, _ = k.shape
+    if rho.shape != q.shape or v.shape != k.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("inconsistent prefill shapes")
+    if not (q.dtype == rho.dtype == k.dtype == v.dtype):
+        raise TypeError("q, rho, k and v must share one dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_prefill(
+            q.data_ptr(), rho.data_ptr(), k.data_ptr(), v.data_ptr(), seq_lens.data_ptr(),
+            out.data_ptr(), B, H_q, H_kv, d, T, S_max, float(scale), _dtype_code(q),
+            _stream_ptr(q.device)), "parallax_prefill")
+    return out

@@ -1,0 +1,255 @@
+// extern "C" entry points of libparallax (declared in include/parallax.h).
+// Host code only: argument checks, split planning and kernel launches on the
+// caller's stream. No allocation, no synchronisation, no exceptions across
+// the boundary.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+
+#include "kernels.h"
+#include "parallax.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not yet queried
+
+// Compute units of the current device, queried once per device.
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int round_up(long long x, int m) { return (int)(((x + m - 1) / m) * m); }
+
+constexpr int kChunkQuantum = 128;  // keys per workgroup pass (4 waves x 32 keys)
+
+// Split plan: chunk (keys per workgroup, multiple of 128) and split count.
+parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* ns_out,
+                       int* chunk_out) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || S_max <= 0 || H_q % H_kv != 0)
+    return PARALLAX_ERR_BAD_SHAPE;
+  const int G = H_q / H_kv;
+  const long long groups = (G + 3) / 4;
+  const long long streams = (long long)B * H_kv * groups;
+  const int full = round_up(S_max, kChunkQuantum);
+  int chunk;
+  if (requested > 0) {
+    chunk = round_up((S_max + (long long)requested - 1) / requested, kChunkQuantum);
+  } else {
+    const int cus = cu_count();
+    if (cus <= 0) return PARALLAX_ERR_HIP;
+    // about four workgroups per compute unit, 256..2048 keys each
+    const long long target = 4LL * cus;
+    long long want = ((long long)S_max * streams + target - 1) / target;
+    chunk = round_up(want, kChunkQuantum);
+    if (chunk < 256) chunk = 256;
+    if (chunk > 2048) chunk = 2048;
+  }
+  if (chunk > full) chunk = full;
+  const int ns = (S_max + chunk - 1) / chunk;
+  if (ns_out) *ns_out = ns;
+  if (chunk_out) *chunk_out = chunk;
+  return PARALLAX_OK;
+}
+
+size_t workspace_bytes_for(int B, int H_q, int d, int ns) {
+  if (B <= 0 || H_q <= 0 || d <= 0 || ns <= 1) return 0;
+  return (size_t)B * H_q * ns * (size_t)(2 * d + 4) * sizeof(float);
+}
+
+struct Checked {
+  parallax::DecodeArgs a;
+  size_t ws_need;
+};
+
+parallax_status_t check_decode(const void* q, const void* rho, const void* k, const void* v,
+                               const int32_t* seq_lens, float* out, bool need_out, int B,
+                               int H_q, int H_kv, int d, int S_max, float scale,
+                               parallax_dtype_t dtype, int num_splits, void* ws,
+                               size_t ws_bytes, Checked* c) {
+  if (!q || !rho || !k || !v || !seq_lens) return PARALLAX_ERR_NULL_POINTER;
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || S_max <= 0 || num_splits < 0 ||
+      H_q % H_kv != 0)
+    return PARALLAX_ERR_BAD_SHAPE;
+  if (dtype != PARALLAX_BF16 && dtype != PARALLAX_F32) return PARALLAX_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
+  const int G = H_q / H_kv;
+  if (G > 4 && G % 4 != 0) return PARALLAX_ERR_UNSUPPORTED;
+  const long long esz = dtype == PARALLAX_F32 ? 4 : 2;
+  if (((long long)S_max + 64) * d * esz >= (1LL << 31)) return PARALLAX_ERR_UNSUPPORTED;
+  if ((long long)H_kv * ((G + 3) / 4) > 65535 || B > 65535) return PARALLAX_ERR_UNSUPPORTED;
+  if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;  // NaN scale
+  if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return PARALLAX_ERR_MISALIGNED;
+  int ns = 0, chunk = 0;
+  parallax_status_t st = plan(B, H_q, H_kv, S_max, num_splits, &ns, &chunk);
+  if (st != PARALLAX_OK) return st;
+  const bool direct = (ns == 1);
+  if ((direct || need_out) && !out) return PARALLAX_ERR_NULL_POINTER;
+  if (out && !aligned16(out)) return PARALLAX_ERR_MISALIGNED;
+  const size_t need = workspace_bytes_for(B, H_q, d, ns);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return PARALLAX_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PARALLAX_ERR_MISALIGNED;
+  }
+  c->ws_need = need;
+  c->a = parallax::DecodeArgs{q, rho, k, v, seq_lens, out, ws, B, H_q, H_kv, G, d, S_max,
+                              ns, chunk, scale, dtype == PARALLAX_F32};
+  return PARALLAX_OK;
+}
+
+parallax_status_t hip_status(hipError_t e) { return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }
+
+const char* parallax_status_string(parallax_status_t s) {
+  switch (s) {
+    case PARALLAX_OK: return "PARALLAX_OK";
+    case PARALLAX_ERR_NULL_POINTER: return "PARALLAX_ERR_NULL_POINTER: a required pointer is NULL";
+    case PARALLAX_ERR_BAD_SHAPE: return "PARALLAX_ERR_BAD_SHAPE: invalid sizes";
+    case PARALLAX_ERR_UNSUPPORTED: return "PARALLAX_ERR_UNSUPPORTED: head dim, group size, dtype or size not built";
+    case PARALLAX_ERR_MISALIGNED: return "PARALLAX_ERR_MISALIGNED: a tensor pointer is not 16-byte aligned";
+    case PARALLAX_ERR_WORKSPACE: return "PARALLAX_ERR_WORKSPACE: workspace missing or too small";
+    case PARALLAX_ERR_HIP: return "PARALLAX_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown parallax status";
+}
+
+parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int S_max, int requested,
+                                       int* num_splits, int* chunk) {
+  try {
+    if (requested < 0) return PARALLAX_ERR_BAD_SHAPE;
+    return plan(B, H_q, H_kv, S_max, requested, num_splits, chunk);
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+size_t parallax_decode_workspace_size(int B, int H_q, int d, int num_splits) {
+  return workspace_bytes_for(B, H_q, d, num_splits);
+}
+
+parallax_status_t parallax_decode_partial(const void* q, const void* rho, const void* k_cache,
+                                          const void* v_cache, const int32_t* seq_lens,
+                                          float* out, int B, int H_q, int H_kv, int d,
+                                          int S_max, float scale, parallax_dtype_t dtype,
+                                          int num_splits, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  try {
+    Checked c;
+    parallax_status_t st = check_decode(q, rho, k_cache, v_cache, seq_lens, out, false, B, H_q,
+                                        H_kv, d, S_max, scale, dtype, num_splits, workspace,
+                                        workspace_bytes, &c);
+    if (st != PARALLAX_OK) return st;
+    return hip_status(parallax::launch_decode_partial(c.a, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+parallax_status_t parallax_decode_combine(const int32_t* seq_lens, float* out, int B, int H_q,
+                                          int H_kv, int d, int S_max, int num_splits,
+                                          const void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  try {
+    if (!seq_lens || !out) return PARALLAX_ERR_NULL_POINTER;
+    if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || S_max <= 0 || num_splits < 0 ||
+        H_q % H_kv != 0)
+      return PARALLAX_ERR_BAD_SHAPE;
+    if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
+    if (!aligned16(out)) return PARALLAX_ERR_MISALIGNED;
+    int ns = 0, chunk = 0;
+    parallax_status_t st = plan(B, H_q, H_kv, S_max, num_splits, &ns, &chunk);
+    if (st != PARALLAX_OK) return st;
+    if (ns == 1) return PARALLAX_OK;
+    const size_t need = workspace_bytes_for(B, H_q, d, ns);
+    if (!workspace || workspace_bytes < need) return PARALLAX_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PARALLAX_ERR_MISALIGNED;
+    parallax::DecodeArgs a{};
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.ws = const_cast<void*>(workspace);
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = H_q / H_kv;
+    a.d = d;
+    a.S_max = S_max;
+    a.num_splits = ns;
+    a.chunk = chunk;
+    return hip_status(parallax::launch_decode_combine(a, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_cache,
+                                  const void* v_cache, const int32_t* seq_lens, float* out,
+                                  int B, int H_q, int H_kv, int d, int S_max, float scale,
+                                  parallax_dtype_t dtype, int num_splits, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  try {
+    Checked c;
+    parallax_status_t st = check_decode(q, rho, k_cache, v_cache, seq_lens, out, true, B, H_q,
+                                        H_kv, d, S_max, scale, dtype, num_splits, workspace,
+                                        workspace_bytes, &c);
+    if (st != PARALLAX_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = parallax::launch_decode_partial(c.a, s);
+    if (e != hipSuccess) return PARALLAX_ERR_HIP;
+    if (c.a.num_splits > 1) e = parallax::launch_decode_combine(c.a, s);
+    return hip_status(e);
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k, const void* v,
+                                   const int32_t* seq_lens, float* out, int B, int H_q, int H_kv,
+                                   int d, int T, int S_max, float scale, parallax_dtype_t dtype,
+                                   void* stream) {
+  try {
+    if (!q || !rho || !k || !v || !seq_lens || !out) return PARALLAX_ERR_NULL_POINTER;
+    if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || T <= 0 || S_max <= 0 || T > S_max ||
+        H_q % H_kv != 0)
+      return PARALLAX_ERR_BAD_SHAPE;
+    if (dtype != PARALLAX_BF16) return PARALLAX_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
+    if (((long long)S_max + 256) * d * 2 >= (1LL << 31) ||
+        ((long long)T + 256) * d * 2 >= (1LL << 31))
+      return PARALLAX_ERR_UNSUPPORTED;
+    if ((long long)B * H_q > 65535LL * 65535LL) return PARALLAX_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+      return PARALLAX_ERR_MISALIGNED;
+    parallax::PrefillArgs a{q, rho, k, v, seq_lens, out, B, H_q, H_kv, H_q / H_kv, d, T, S_max,
+                            scale};
+    return hip_status(parallax::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+}  // extern "C"

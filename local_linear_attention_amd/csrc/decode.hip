@@ -1,0 +1,407 @@
+// Parallax decode on CDNA4 (gfx950): split-KV partial kernel and combine kernel.
+//
+// What is computed (paper page "Parallax: Parameterized Local Linear Attention
+// for Language Modeling", "Abstract"; blog "Parallax: Breaking the Boundary
+// Bias with Parameterized Local Linear Attention", "The Core Insight:
+// Covariance Correction", output equation; "Hardware Efficiency": softmax
+// and covariance branches fused into one pass over the KV stream):
+//
+//   out = mu_v - S_KV rho,  S_KV = sum_i w_i (v_i - mu_v)(k_i - mu_k)^T.
+//
+// Applying S_KV to rho key by key gives a streaming form. With
+// r_i = rho . k_i, e_i = exp(s_i - m), l = sum e_i, A = sum e_i v_i,
+// Bs = sum e_i r_i and C = sum e_i r_i v_i:
+//
+//   S_KV rho = sum_i w_i r_i v_i - (rho . mu_k) mu_v = C/l - (Bs/l)(A/l)
+//   out      = (A (1 + Bs/l) - C) / l.
+//
+// Replacing r_i by r_i - c for any constant c leaves `out` unchanged
+// (Bs -> Bs - c l, C -> C - c A), so each wave accumulates r relative to the
+// r of the first key it sees; this removes any large common offset of
+// rho . k before it can cancel. Partial states with different max (m) and
+// reference (c) merge exactly: rescale by exp(m_j - M) and shift by
+// (c_j - c) as above, an associative and commutative merge.
+//
+// Work layout. A workgroup of 4 waves owns one (b, KV head, group of <= 4
+// query heads, key range of `chunk` keys). Each wave takes every 4th block
+// of 32 keys. Per block a lane loads its K and V pieces straight from HBM into
+// registers with range-checked buffer loads (rows at or past the sequence
+// length come back as zeros, so padding is never read), and two MFMA
+// contractions do the arithmetic:
+//   scores:  [32 keys x d] x [d x 16 probe columns] with v_mfma_f32_16x16x32_bf16,
+//            probe column 4h+t holds q_h for t in {0,1} and rho_h for t in {2,3},
+//            so one pass gives s and r for all (up to 4) heads of the group;
+//   values:  [16 rows x 32 keys] x [32 keys x d], rows 4h+t holding, for head h,
+//            e (t=0,1) or e*(r-c) (t=2,3) split into a bf16 high part (t even)
+//            and the bf16 rounding of the remainder (t odd), so the fp32
+//            weights survive the bf16 contraction to about 2^-17.
+// The score accumulator layout of the MFMA puts, in lane (g = lane/16,
+// c = lane%16), the values of probe column c for keys 16T + 4g + i
+// (T = 0, 1; i = 0..3): exactly the 8 key slots that lane must supply as the
+// A operand of the value MFMA, so no data moves between lanes except one DPP
+// quad permute that hands s to the lanes holding r. V needs no transpose: the
+// lane loads 8 rows x (d/16) contiguous elements and hands element j of each
+// row to N-tile j (value column c of tile j is dimension (d/16) c + j).
+// fp32 inputs are split into bf16 high and low parts and contracted as
+// hi*hi + hi*lo + lo*hi (scores) and P*(v_hi + v_lo) (values).
+// The softmax max is rescaled lazily: only when a block's max exceeds the
+// running reference by more than 2^8, which keeps every exp below 256.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace parallax {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBlockKeys = 32;
+constexpr float kRescaleLog2 = 8.0f;
+
+template <typename T, int D>
+struct Dec {
+  static constexpr int ESZ = sizeof(T);
+  static constexpr int ROWB = D * ESZ;                  // bytes per K/V row
+  static constexpr int KSTEPS = D / 32;                 // score MFMA k-steps
+  static constexpr int DPL = D / 16;                    // value dims per lane = N-tiles
+  static constexpr int KW = 8 * ESZ / 4;                // words per K piece (8 elements)
+  static constexpr int VW = DPL * ESZ / 4;              // words per V row piece
+  static constexpr bool F32 = (ESZ == 4);
+  static constexpr int REC = 2 * D + 4;                 // fp32 words per partial record
+};
+
+// 8 consecutive elements (one MFMA operand) from words; fp32 gives hi and lo.
+template <typename T>
+__device__ __forceinline__ void to_operand(const uint32_t* w, bf16x8& hi, bf16x8& lo) {
+  if constexpr (sizeof(T) == 2) {
+    hi = as_bf16x8(w[0], w[1], w[2], w[3]);
+  } else {
+    float x[8], r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = __uint_as_float(w[i]);
+      r[i] = x[i] - bf16_round(x[i]);
+    }
+    hi = as_bf16x8(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                   pack_bf16(x[6], x[7]));
+    lo = as_bf16x8(pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]), pack_bf16(r[4], r[5]),
+                   pack_bf16(r[6], r[7]));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t load_probe_words(const T* p, int n, uint32_t* w) {
+  // 8 elements at p (16-byte aligned); n words
+  const uint4* src = reinterpret_cast<const uint4*>(p);
+  uint4 a = src[0];
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  if (n == 8) {
+    uint4 b = src[1];
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+  return 0;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ rho, const T* __restrict__ kc,
+    const T* __restrict__ vc, const int32_t* __restrict__ seq_lens, float* __restrict__ out,
+    float* __restrict__ ws, int H_q, int H_kv, int G, int S_max, int chunk, int num_splits,
+    float scale_log2) {
+  using P = Dec<T, D>;
+  __shared__ float lds_state[kWaves][4][4];          // m, l, bs, cref per head
+  __shared__ float lds_vec[kWaves][2][4][D];         // A, C per head
+
+  const int split = blockIdx.x;
+  const int ngroups = (G + 3) / 4;
+  const int hk = blockIdx.y / ngroups;
+  const int hgrp = blockIdx.y % ngroups;
+  const int b = blockIdx.z;
+  const int Gw = min(4, G - 4 * hgrp);               // heads in this workgroup
+  const int h0 = hk * G + 4 * hgrp;                  // first query head
+
+  const int n = min(max(seq_lens[b], 0), S_max);
+  const int j0 = split * chunk;
+  const bool direct = (num_splits == 1);
+  if (j0 >= n && !direct) return;                    // empty split: combine skips it
+  const int j1 = min(j0 + chunk, n);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 4;                           // lane group (0..3)
+  const int c = lane & 15;                           // lane column (0..15)
+  const int hq = c >> 2;                             // head whose scores this lane holds
+  const int t = c & 3;                               // 0,1: q / e rows; 2,3: rho / e*r rows
+
+  // Probe operand (B of the score MFMA): column c, dims 32 kk + 8 g + (0..7).
+  bf16x8 pr_hi[P::KSTEPS], pr_lo[P::KSTEPS];
+  {
+    const bool live = hq < Gw;
+    const T* src = (t < 2 ? q : rho) + ((size_t)b * H_q + h0 + (live ? hq : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < P::KSTEPS; ++kk) {
+      uint32_t w[P::KW];
+      load_probe_words<T>(src + 32 * kk + 8 * g, P::KW, w);
+      if (!live) {
+#pragma unroll
+        for (int i = 0; i < P::KW; ++i) w[i] = 0;
+      }
+      to_operand<T>(w, pr_hi[kk], pr_lo[kk]);
+    }
+  }
+
+  const size_t slice = ((size_t)b * H_kv + hk) * (size_t)S_max * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + slice, (uint32_t)n * P::ROWB);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + slice, (uint32_t)n * P::ROWB);
+
+  f32x4 acc[P::DPL];
+#pragma unroll
+  for (int j = 0; j < P::DPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // running max (log2 units) for head hq
+  float lsum = 0.f;     // this lane's partial of l (t == 0) or Bs (t == 2)
+  float cref = 0.f;     // probe reference for head hq
+  bool first = true;
+
+  for (int blk = j0 + kBlockKeys * wave; blk < j1; blk += kBlockKeys * kWaves) {
+    // ---- loads: K pieces for the score MFMA, V rows for the value MFMA
+    Words<P::KW> kw[2][P::KSTEPS];
+#pragma unroll
+    for (int T2 = 0; T2 < 2; ++T2)
+#pragma unroll
+      for (int kk = 0; kk < P::KSTEPS; ++kk)
+        kw[T2][kk] = buffer_load<P::KW>(
+            krs, (uint32_t)(blk + 16 * T2 + c) * P::ROWB + (32 * kk + 8 * g) * P::ESZ);
+    Words<P::VW> vw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vw[e] = buffer_load<P::VW>(
+          vrs, (uint32_t)(blk + 16 * (e >> 2) + 4 * g + (e & 3)) * P::ROWB + P::DPL * c * P::ESZ);
+
+    // ---- scores: lane (g, c) gets probe column c for keys 16 T2 + 4 g + i
+    f32x4 sc[2];
+#pragma unroll
+    for (int T2 = 0; T2 < 2; ++T2) {
+      sc[T2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < P::KSTEPS; ++kk) {
+        bf16x8 khi, klo;
+        to_operand<T>(kw[T2][kk].w, khi, klo);
+        sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_hi[kk], sc[T2], 0, 0, 0);
+        if constexpr (P::F32) {
+          sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_lo[kk], sc[T2], 0, 0, 0);
+          sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, pr_hi[kk], sc[T2], 0, 0, 0);
+        }
+      }
+    }
+
+    float x[8], rv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float raw = sc[e >> 2][e & 3];
+      const int key = blk + 16 * (e >> 2) + 4 * g + (e & 3);
+      float s = quad_perm_0101(raw) * scale_log2;
+      s = key < j1 ? s : -INFINITY;
+      x[e] = s;
+      rv[e] = raw;
+      mx = fmaxf(mx, s);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    if (first) {
+      // reference: r of the first key of this wave's first block (lane 4h+2, slot 0)
+      cref = __shfl(rv[0], 4 * hq + 2);
+      first = false;
+    }
+
+    const bool need = mx > m + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mnew = need ? mx : m;
+      const float alpha = need ? exp2f(m - mnew) : 1.0f;
+      m = mnew;
+      lsum *= alpha;
+      const float a_acc = __shfl(alpha, 4 * g);  // accumulator rows belong to head g
+#pragma unroll
+      for (int j = 0; j < P::DPL; ++j) acc[j] *= a_acc;
+    }
+
+    // ---- value-MFMA A operand: row c = 4h + t, key slots (g, e)
+    uint32_t aw[4];
+    {
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2f(x[e] - m);
+        float val = t >= 2 ? p * (rv[e] - cref) : p;
+        val = hq < Gw ? val : 0.f;
+        lsum += val;
+        const float hi = bf16_round(val);
+        a[e] = (t & 1) ? val - hi : val;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) aw[u] = pack_bf16(a[2 * u], a[2 * u + 1]);
+    }
+    const bf16x8 aop = as_bf16x8(aw[0], aw[1], aw[2], aw[3]);
+
+    // ---- values: N-tile j covers dims (d/16) c + j
+#pragma unroll
+    for (int j = 0; j < P::DPL; ++j) {
+      if constexpr (!P::F32) {
+        uint32_t bw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          bw[u] = pair_halves(vw[2 * u].w[j >> 1], vw[2 * u + 1].w[j >> 1], j & 1);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, as_bf16x8(bw[0], bw[1], bw[2], bw[3]),
+                                                         acc[j], 0, 0, 0);
+      } else {
+        float vv[8], vr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          vv[e] = __uint_as_float(vw[e].w[j]);
+          vr[e] = vv[e] - bf16_round(vv[e]);
+        }
+        const bf16x8 bhi = as_bf16x8(pack_bf16(vv[0], vv[1]), pack_bf16(vv[2], vv[3]),
+                                     pack_bf16(vv[4], vv[5]), pack_bf16(vv[6], vv[7]));
+        const bf16x8 blo = as_bf16x8(pack_bf16(vr[0], vr[1]), pack_bf16(vr[2], vr[3]),
+                                     pack_bf16(vr[4], vr[5]), pack_bf16(vr[6], vr[7]));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bhi, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, blo, acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- per-wave state to LDS
+  float tot = lsum + __shfl_xor(lsum, 16);
+  tot += __shfl_xor(tot, 32);
+  if (g == 0 && hq < 4) {
+    if (t == 0) {
+      lds_state[wave][hq][0] = m;
+      lds_state[wave][hq][1] = first ? 0.f : tot;
+      lds_state[wave][hq][3] = cref;
+    } else if (t == 2) {
+      lds_state[wave][hq][2] = first ? 0.f : tot;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < P::DPL; ++j) {
+    lds_vec[wave][0][g][P::DPL * c + j] = acc[j][0] + acc[j][1];
+    lds_vec[wave][1][g][P::DPL * c + j] = acc[j][2] + acc[j][3];
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves; finalise (one split) or write the partial record
+  for (int idx = tid; idx < Gw * D; idx += 256) {
+    const int h = idx / D;
+    const int dim = idx % D;
+    float M = -INFINITY;
+    float c0 = 0.f;
+    bool have = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (lds_state[w][h][1] > 0.f) {
+        if (!have) c0 = lds_state[w][h][3];
+        have = true;
+        M = fmaxf(M, lds_state[w][h][0]);
+      }
+    }
+    float l = 0.f, bs = 0.f, A = 0.f, C = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float lw = lds_state[w][h][1];
+      if (lw > 0.f) {
+        const float al = exp2f(lds_state[w][h][0] - M);
+        const float sh = lds_state[w][h][3] - c0;
+        const float Aw = lds_vec[w][0][h][dim];
+        l += al * lw;
+        bs += al * (lds_state[w][h][2] + sh * lw);
+        A += al * Aw;
+        C += al * (lds_vec[w][1][h][dim] + sh * Aw);
+      }
+    }
+    if (direct) {
+      out[((size_t)b * H_q + h0 + h) * D + dim] = l > 0.f ? (A * (1.f + bs / l) - C) / l : 0.f;
+    } else {
+      float* rec = ws + (((size_t)b * H_q + h0 + h) * num_splits + split) * P::REC;
+      if (dim == 0) {
+        rec[0] = M;
+        rec[1] = l;
+        rec[2] = bs;
+        rec[3] = c0;
+      }
+      rec[4 + dim] = A;
+      rec[4 + D + dim] = C;
+    }
+  }
+}
+
+// One workgroup of D threads per (b, h_q): merges the partial records of the
+// splits that hold keys and writes out[b, h_q, :].
+template <int D>
+__global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __restrict__ seq_lens,
+                                                             const float* __restrict__ ws,
+                                                             float* __restrict__ out, int H_q,
+                                                             int S_max, int chunk, int num_splits) {
+  constexpr int REC = 2 * D + 4;
+  const int bh = blockIdx.x;
+  const int b = bh / H_q;
+  const int dim = threadIdx.x;
+  const int n = min(max(seq_lens[b], 0), S_max);
+  const int nsv = min(num_splits, (n + chunk - 1) / chunk);
+  const float* base = ws + (size_t)bh * num_splits * REC;
+  float M = -INFINITY;
+  for (int s = 0; s < nsv; ++s) M = fmaxf(M, base[(size_t)s * REC]);
+  const float c0 = nsv > 0 ? base[3] : 0.f;
+  float l = 0.f, bs = 0.f, A = 0.f, C = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < nsv; ++s) {
+    const float* rec = base + (size_t)s * REC;
+    const float al = exp2f(rec[0] - M);
+    const float lw = rec[1];
+    const float sh = rec[3] - c0;
+    const float Aw = rec[4 + dim];
+    l += al * lw;
+    bs += al * (rec[2] + sh * lw);
+    A += al * Aw;
+    C += al * (rec[4 + D + dim] + sh * Aw);
+  }
+  out[(size_t)bh * D + dim] = l > 0.f ? (A * (1.f + bs / l) - C) / l : 0.f;
+}
+
+template <typename T, int D>
+hipError_t launch_partial_t(const DecodeArgs& a, hipStream_t st) {
+  const int ngroups = (a.G + 3) / 4;
+  dim3 grid(a.num_splits, a.H_kv * ngroups, a.B);
+  hipLaunchKernelGGL((decode_partial_kernel<T, D>), grid, dim3(256), 0, st,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.rho),
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.seq_lens, a.out,
+                     static_cast<float*>(a.ws), a.H_q, a.H_kv, a.G, a.S_max, a.chunk,
+                     a.num_splits, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st) {
+  if (a.f32) {
+    return a.d == 64 ? launch_partial_t<float, 64>(a, st) : launch_partial_t<float, 128>(a, st);
+  }
+  return a.d == 64 ? launch_partial_t<__bf16, 64>(a, st) : launch_partial_t<__bf16, 128>(a, st);
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
+  dim3 grid(a.B * a.H_q);
+  if (a.d == 64) {
+    hipLaunchKernelGGL((decode_combine_kernel<64>), grid, dim3(64), 0, st, a.seq_lens,
+                       static_cast<const float*>(a.ws), a.out, a.H_q, a.S_max, a.chunk,
+                       a.num_splits);
+  } else {
+    hipLaunchKernelGGL((decode_combine_kernel<128>), grid, dim3(128), 0, st, a.seq_lens,
+                       static_cast<const float*>(a.ws), a.out, a.H_q, a.S_max, a.chunk,
+                       a.num_splits);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace parallax

@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+The fake device pointers below are never dereferenced: each call returns an
+error status from the host-side checks, which run before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import local_linear_attention_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "parallax.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, WS, HIP = range(7)
+BF16, F32 = 0, 1
+P = 0x10000  # 16-byte aligned fake device address
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pa.library_path()):
+        from local_linear_attention_amd.build import build
+
+        build()
+    return pa.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(parallax_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(L):
+    names = header_functions()
+    assert len(names) == 8
+    assert set(names) == set(pa.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version(L):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define PARALLAX_ABI_VERSION (\d+)", text).group(1))
+    assert pa.abi_version() == v
+
+
+def test_status_strings(L):
+    for code, name in pa.STATUS.items():
+        assert pa.status_string(code).startswith(name)
+    assert "unknown" in pa.status_string(99)
+
+
+def _plan(L, B, Hq, Hkv, S, req):
+    ns, ch = ctypes.c_int(-1), ctypes.c_int(-1)
+    st = L.parallax_decode_plan(B, Hq, Hkv, S, req, ctypes.byref(ns), ctypes.byref(ch))
+    return st, ns.value, ch.value
+
+
+def test_plan_requested(L):
+    assert _plan(L, 8, 16, 8, 4096, 16) == (OK, 16, 256)
+    assert _plan(L, 8, 16, 8, 4096, 1) == (OK, 1, 4096)
+    assert _plan(L, 1, 32, 8, 131072, 128) == (OK, 128, 1024)
+    st, ns, ch = _plan(L, 1, 1, 1, 100, 7)  # chunk rounds to 128 -> one split
+    assert (st, ns, ch) == (OK, 1, 128)
+    st, ns, ch = _plan(L, 2, 4, 2, 1000, 3)
+    assert st == OK and ch % 128 == 0 and ns * ch >= 1000 and (ns - 1) * ch < 1000
+
+
+def test_plan_bad_shapes(L):
+    for args in [(0, 1, 1, 10, 1), (1, 3, 2, 10, 1), (1, 2, 2, 0, 1), (1, 2, 2, 10, -1)]:
+        assert _plan(L, *args)[0] == SHAPE
+
+
+def test_workspace_size(L):
+    assert pa.decode_workspace_size(8, 16, 128, 16) == 8 * 16 * 16 * 260 * 4
+    assert pa.decode_workspace_size(8, 16, 128, 1) == 0
+    assert pa.decode_workspace_size(0, 16, 128, 4) == 0
+
+
+def _decode(L, fn="parallax_decode", q=P, rho=P, k=P, v=P, lens=P, out=P, B=2, Hq=4, Hkv=2,
+            d=128, S=512, scale=1.0, dtype=BF16, ns=2, ws=P, ws_bytes=1 << 30):
+    return getattr(L, fn)(q, rho, k, v, lens, out, B, Hq, Hkv, d, S, scale, dtype, ns, ws,
+                          ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["parallax_decode", "parallax_decode_partial"])
+def test_decode_argument_errors(L, fn):
+    assert _decode(L, fn, q=0) == NULLP
+    assert _decode(L, fn, lens=0) == NULLP
+    assert _decode(L, fn, B=0) == SHAPE
+    assert _decode(L, fn, Hq=3, Hkv=2) == SHAPE
+    assert _decode(L, fn, ns=-1) == SHAPE
+    assert _decode(L, fn, scale=float("nan")) == SHAPE
+    assert _decode(L, fn, d=96) == UNSUP
+    assert _decode(L, fn, dtype=7) == UNSUP
+    assert _decode(L, fn, Hq=6, Hkv=1) == UNSUP  # G = 6: not <= 4 and not a multiple of 4
+    assert _decode(L, fn, S=1 << 24) == UNSUP    # a (b, h_kv) slice of 4 GiB
+    assert _decode(L, fn, k=P + 8) == MISAL
+    assert _decode(L, fn, lens=P + 2) == MISAL
+    assert _decode(L, fn, ws=0) == WS
+    assert _decode(L, fn, ws_bytes=100) == WS
+    assert _decode(L, fn, ws=P + 4) == MISAL
+    assert _decode(L, fn, out=P + 4) == MISAL
+
+
+def test_decode_out_required(L):
+    assert _decode(L, "parallax_decode", out=0) == NULLP
+    # one split: the partial kernel finalises into out, so out is required
+    assert _decode(L, "parallax_decode_partial", out=0, ns=1, S=128) == NULLP
+
+
+def test_combine_argument_errors(L):
+    f = L.parallax_decode_combine
+    assert f(0, P, 2, 4, 2, 128, 512, 2, P, 1 << 30, None) == NULLP
+    assert f(P, 0, 2, 4, 2, 128, 512, 2, P, 1 << 30, None) == NULLP
+    assert f(P, P, 2, 3, 2, 128, 512, 2, P, 1 << 30, None) == SHAPE
+    assert f(P, P, 2, 4, 2, 80, 512, 2, P, 1 << 30, None) == UNSUP
+    assert f(P, P + 4, 2, 4, 2, 128, 512, 2, P, 1 << 30, None) == MISAL
+    assert f(P, P, 2, 4, 2, 128, 512, 2, 0, 1 << 30, None) == WS
+    assert f(P, P, 2, 4, 2, 128, 512, 2, P, 64, None) == WS
+    # one split: nothing to merge, returns OK without launching
+    assert f(P, P, 2, 4, 2, 128, 128, 1, 0, 0, None) == OK
+
+
+def _prefill(L, q=P, rho=P, k=P, v=P, lens=P, out=P, B=2, Hq=4, Hkv=2, d=128, T=256, S=256,
+             scale=1.0, dtype=BF16):
+    return L.parallax_prefill(q, rho, k, v, lens, out, B, Hq, Hkv, d, T, S, scale, dtype, None)
+
+
+def test_prefill_argument_errors(L):
+    assert _prefill(L, out=0) == NULLP
+    assert _prefill(L, v=0) == NULLP
+    assert _prefill(L, T=0) == SHAPE
+    assert _prefill(L, T=300, S=256) == SHAPE
+    assert _prefill(L, Hq=5, Hkv=2) == SHAPE
+    assert _prefill(L, scale=float("nan")) == SHAPE
+    assert _prefill(L, dtype=F32) == UNSUP
+    assert _prefill(L, d=32) == UNSUP
+    assert _prefill(L, q=P + 2) == MISAL
+    assert _prefill(L, out=P + 8) == MISAL
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    t = torch.zeros(1, 1, 64)
+    with pytest.raises(ValueError):
+        pa.decode(t, t, t[None], t[None], torch.ones(1, dtype=torch.int32), 1.0)
