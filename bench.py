@@ -1,0 +1,326 @@
+"""Benchmark of the Parallax forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|main]
+
+A step is one pass of the decode hot path (one launch of the split-KV decode
+kernel, whose last workgroup per stream merges the partial states) over one
+batch of the GQA decode workload (B=8, H_q=16,
+H_kv=8, d=128, 4096 keys per sequence, bf16). The KV cache is held in 8
+copies in HBM (1.07 GB) and step i reads copy i mod 8, so no step finds its
+134 MB stream in the 256 MB Infinity Cache left there by the previous one.
+K timed steps are bracketed by device synchronisations; `value` is the KV
+stream (algorithmic bytes: every valid K and V row once) divided by the
+mean step time. A step is a single kernel launch, so a pair of HIP events on
+the launch stream around the timed region, divided by K, gives the kernel's
+average launch duration for the `roofline` object. The other workloads (single-head fp32, ragged batch,
+128K-context split-KV decode, causal prefill) are timed the same way, briefly,
+and reported under "workloads". The `cpu_baseline` leg times the fp64 oracle
+on a bounded sample of the same GQA decode workload on the host cores.
+
+One JSON line is printed at the end.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-stream HBM GB/s (% of peak) + us/step; prefill MFMA util"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """Digest of the decode kernel sources (ties counter figures to a build)."""
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "local_linear_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed counter summary.
+
+    Returns None when there is no summary or the kernel source changed since
+    the counters were taken.
+    """
+    path = os.path.join(PROFILE_DIR, f"decode_partial_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_digest():
+        return None
+    vals = {}
+    for key in ("fetch_bytes_per_launch", "write_bytes_per_launch"):
+        mm = re.search(key + r":\s*([0-9.eE+]+)", text)
+        if not mm:
+            return None
+        vals[key] = float(mm.group(1))
+    return vals
+
+
+class DecodeRunner:
+    """Holds device buffers and pre-marshalled C-ABI arguments for one workload."""
+
+    def __init__(self, w, nbuf, seed=None, num_splits=0):
+        import torch
+
+        import local_linear_attention_amd as pa
+        from workloads import make_decode_inputs
+
+        self.torch = torch
+        self.w = w
+        dev = torch.device("cuda:0")
+        inp = make_decode_inputs(w, seed=seed, device=dev)
+        self.inp = inp
+        self.lens = inp["seq_lens"].cpu().tolist()
+        self.kv_bytes = w.kv_bytes(self.lens)
+        ks, vs = [inp["k_cache"]], [inp["v_cache"]]
+        for _ in range(nbuf - 1):
+            ks.append(inp["k_cache"].clone())
+            vs.append(inp["v_cache"].clone())
+        self.ks, self.vs = ks, vs
+        self.ns, self.chunk = pa.decode_plan(w.B, w.H_q, w.H_kv, w.S_max, num_splits)
+        ws_bytes = max(pa.decode_workspace_size(w.B, w.H_q, w.d, self.ns), 16)
+        self.ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device=dev)
+        self.out = torch.empty((w.B, w.H_q, w.d), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+        self.L = pa.lib()
+        dcode = 0 if w.dtype == torch.bfloat16 else 1
+        self.pargs = [
+            (inp["q"].data_ptr(), inp["rho"].data_ptr(), k.data_ptr(), v.data_ptr(),
+             inp["seq_lens"].data_ptr(), self.out.data_ptr(), w.B, w.H_q, w.H_kv, w.d, w.S_max,
+             float(inp["scale"]), dcode, self.ns, self.ws.data_ptr(), ws_bytes, self.stream)
+            for k, v in zip(ks, vs)]
+
+    def step(self, i):
+        st = self.L.parallax_decode(*self.pargs[i % len(self.pargs)])
+        if st != 0:
+            raise RuntimeError(f"decode failed with status {st}")
+
+    def run(self, steps, warmup):
+        """(wall seconds per step, event-timed seconds per decode launch).
+
+        A step is one decode launch, so the event pair recorded on the launch
+        stream around the whole timed region, divided by the step count, is
+        the kernel's average launch duration (back-to-back launches).
+        """
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record()
+        for i in range(steps):
+            self.step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) / steps, ev0.elapsed_time(ev1) / steps / 1e3
+
+
+def bench_prefill(w, steps, warmup, seed=None):
+    import torch
+
+    import local_linear_attention_amd as pa
+    from workloads import make_prefill_inputs
+
+    dev = torch.device("cuda:0")
+    inp = make_prefill_inputs(w, seed=seed, device=dev)
+    out = torch.empty((w.B, w.H_q, w.T, w.d), dtype=torch.float32, device=dev)
+    L = pa.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = (inp["q"].data_ptr(), inp["rho"].data_ptr(), inp["k"].data_ptr(), inp["v"].data_ptr(),
+            inp["seq_lens"].data_ptr(), out.data_ptr(), w.B, w.H_q, w.H_kv, w.d, w.T,
+            inp["k"].shape[2], float(inp["scale"]), 0, stream)
+    for _ in range(warmup):
+        if L.parallax_prefill(*args) != 0:
+            raise RuntimeError("prefill failed")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        L.parallax_prefill(*args)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = ev0.elapsed_time(ev1) / steps / 1e3
+    # algorithmic work: q.k, rho.k, e.v and (e r).v over the causal half, 2 d flops each
+    flops = 8.0 * w.d * (w.T * (w.T + 1) / 2) * w.B * w.H_q
+    return {"us_per_step": (t1 - t0) / steps * 1e6, "kernel_us": kern * 1e6,
+            "algorithmic_tflop": flops / 1e12, "tflops": flops / kern / 1e12,
+            "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
+
+
+def cpu_baseline(runner, budget_s=15.0):
+    """Times the fp64 oracle on a bounded sample of the GQA decode workload."""
+    import numpy as np
+
+    import oracle
+    from oracle.parallax_oracle import _f64
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    w = runner.w
+    inp = runner.inp
+    G = w.H_q // w.H_kv
+    got = runner.out.cpu().numpy()
+    q = inp["q"].cpu()
+    rho = inp["rho"].cpu()
+    done = 0
+    t_total = 0.0
+    err = 0.0
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H_q)]
+    for b, h in pairs:
+        n = runner.lens[b]
+        K = _f64(inp["k_cache"][b, h // G, :n].cpu())
+        V = _f64(inp["v_cache"][b, h // G, :n].cpu())
+        qq, rr = _f64(q[b, h]), _f64(rho[b, h])
+        t0 = time.perf_counter()
+        o = oracle.parallax_attend(qq, rr, K, V, inp["scale"])
+        t_total += time.perf_counter() - t0
+        done += 1
+        err = max(err, float(np.abs(got[b, h] - o).max() / np.abs(o).max()))
+        if t_total > budget_s:
+            break
+    frac = done / len(pairs)
+    gbs = runner.kv_bytes * frac / t_total / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} query heads of the gqa-decode workload "
+                      f"(fp64 NumPy, explicit d x d Sigma_KV), {t_total:.1f} s; "
+                      f"GB/s counts the same fraction of the workload's KV stream",
+            "seconds": t_total, "gpu_vs_oracle_max_rel_err": err,
+            "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workloads", choices=["all", "main"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode "
+              f"path shards by (batch, KV head) with no exchange, so N GPUs run N "
+              f"independent copies of this measurement.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    w = WORKLOADS[2]
+    log(f"main workload {w.name}")
+    main_r = DecodeRunner(w, nbuf=8)
+    step_s, part_s = main_r.run(args.steps, args.warmup)
+    gbs = main_r.kv_bytes / step_s / 1e9
+    part_gbs = main_r.kv_bytes / part_s / 1e9
+    traffic = read_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k~N(0,1)/d^0.25, v~N(0,1), rho~N(0,0.05^2), bf16)",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "d": w.d,
+                   "kv_len": w.S_max, "num_splits": main_r.ns, "chunk": main_r.chunk,
+                   "kv_bytes": main_r.kv_bytes, "kv_copies_rotated": 8},
+        "us_per_step": step_s * 1e6,
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_partial_kernel<bf16,128> (fused merge)",
+            "achieved": round(part_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": main_r.kv_bytes,
+            "kernel_us": part_s * 1e6,
+            "traffic": None if traffic is None else
+            int(traffic["fetch_bytes_per_launch"] + traffic["write_bytes_per_launch"]),
+            "traffic_fetch_bytes": None if traffic is None else int(traffic["fetch_bytes_per_launch"]),
+            "traffic_write_bytes": None if traffic is None else int(traffic["write_bytes_per_launch"]),
+        },
+    }
+    log(f"{w.name}: {gbs:.0f} GB/s per step, decode kernel {part_gbs:.0f} GB/s")
+
+    workloads = {}
+    if args.workloads == "all":
+        for idx, nbuf in ((1, 1), (3, 1), (4, 2)):
+            wi = WORKLOADS[idx]
+            log(f"workload {wi.name}")
+            r = DecodeRunner(wi, nbuf=nbuf)
+            ksteps = max(10, args.steps // (10 if idx == 3 else 2))
+            s, p = r.run(ksteps, max(3, args.warmup // 4))
+            workloads[wi.name] = {
+                "us_per_step": s * 1e6, "kernel_us": p * 1e6,
+                "kv_bytes": r.kv_bytes, "GB_per_s": r.kv_bytes / s / 1e9,
+                "pct_of_hbm_peak": 100 * r.kv_bytes / s / 1e9 / HBM_PEAK_GBS,
+                "num_splits": r.ns, "chunk": r.chunk, "steps": ksteps,
+                "dtype": "f32" if idx == 1 else "bf16"}
+            del r
+            torch.cuda.empty_cache()
+        log("workload causal-prefill")
+        try:
+            workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 3)
+        except RuntimeError as e:
+            workloads[WORKLOADS[5].name] = {"error": str(e)}
+    result["workloads"] = workloads
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(main_r)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -92,8 +92,15 @@ parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int S_max, int 
  * Workspace bytes needed by parallax_decode / parallax_decode_partial for the
  * plan `num_splits` (as returned by parallax_decode_plan): one fp32 record of
  * (2 d + 4) values (running max, weight sum, probe sum, probe reference, and
- * two d-vectors) per (b, h_q, split). 0 if num_splits == 1 (the partial kernel
- * then finalises directly) or on a bad shape.
+ * two d-vectors) per (b, h_q, split), followed by B * H_q 32-bit arrival
+ * counters (rounded up to 16 bytes). 0 if num_splits == 1 (the kernel then
+ * finalises directly) or on a bad shape.
+ *
+ * The counters are used by parallax_decode only. They must be zero before the
+ * first parallax_decode call on a workspace (allocate it zeroed, or clear the
+ * whole workspace once); every call returns them to zero. Calls that share a
+ * workspace must be ordered (same stream or synchronised): overlapping calls
+ * on one workspace race.
  */
 size_t parallax_decode_workspace_size(int B, int H_q, int d, int num_splits);
 
@@ -108,8 +115,12 @@ size_t parallax_decode_workspace_size(int B, int H_q, int d, int num_splits);
  *   num_splits 0 = automatic plan, else the requested split count
  *   workspace  device scratch of at least parallax_decode_workspace_size()
  *              bytes for the resolved plan (may be NULL when that is 0)
- * Equivalent to parallax_decode_partial followed by parallax_decode_combine
- * (a single launch when the plan has one split).
+ * One kernel launch: each workgroup streams its key range once; with several
+ * splits, the last workgroup to finish for each (b, KV head, group of query
+ * heads) merges the partial states (same result as parallax_decode_partial
+ * followed by parallax_decode_combine, up to rounding). With several splits
+ * the workspace's counters must be zero on entry (see
+ * parallax_decode_workspace_size); they are zero again on exit.
  */
 parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_cache,
                                   const void* v_cache, const int32_t* seq_lens, float* out,
@@ -121,7 +132,7 @@ parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_
  * First phase of decode: streams every valid K/V row once and writes one
  * partial state per (b, h_q, split) to `workspace` (or, when the resolved
  * plan has one split, finalises straight into `out`, which may otherwise be
- * NULL). Arguments as parallax_decode.
+ * NULL). Arguments as parallax_decode. Does not use the workspace counters.
  */
 parallax_status_t parallax_decode_partial(const void* q, const void* rho, const void* k_cache,
                                           const void* v_cache, const int32_t* seq_lens,

@@ -67,7 +67,13 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(
             f"{_LIB_PATH} is missing: build it with `python -m local_linear_attention_amd.build`")
-    L = ctypes.CDLL(_LIB_PATH)
+    _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Loads a libparallax build from ``path`` and declares its C signatures."""
+    L = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.parallax_abi_version.restype = i
     L.parallax_abi_version.argtypes = []
@@ -86,7 +92,6 @@ def lib() -> ctypes.CDLL:
     L.parallax_decode_combine.argtypes = [vp, vp, i, i, i, i, i, i, vp, sz, vp]
     L.parallax_prefill.restype = i
     L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
-    _lib = L
     return L
 
 
@@ -156,7 +161,8 @@ def _workspace(B, H_q, H_kv, d, S_max, num_splits, workspace, device):
     ns, _ = decode_plan(B, H_q, H_kv, S_max, num_splits)
     need = decode_workspace_size(B, H_q, d, ns)
     if workspace is None:
-        workspace = torch.empty(max(need, 16) // 4 + 1, dtype=torch.float32, device=device)
+        # zeroed: the fused merge's arrival counters must start at zero
+        workspace = torch.zeros(max(need, 16) // 4, dtype=torch.float32, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 

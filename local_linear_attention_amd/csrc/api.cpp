@@ -38,6 +38,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int round_up(long long x, int m) { return (int)(((x + m - 1) / m) * m); }
 
 constexpr int kChunkQuantum = 128;  // keys per workgroup pass (4 waves x 32 keys)
+constexpr int kMaxAutoSplits = 32;  // automatic plans use at most this many splits
 
 // Split plan: chunk (keys per workgroup, multiple of 128) and split count.
 parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* ns_out,
@@ -54,12 +55,18 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
   } else {
     const int cus = cu_count();
     if (cus <= 0) return PARALLAX_ERR_HIP;
-    // about four workgroups per compute unit, 256..2048 keys each
-    const long long target = 4LL * cus;
+    // About two workgroups per compute unit over the padded key range, with
+    // chunks of 512..2048 keys (one 4-wave workgroup per CU already saturates
+    // HBM on this access pattern; the cap keeps ragged batches balanced), but
+    // at most 32 splits per stream, since the fused merge reads every split's
+    // record and its cost grows with the split count.
+    const long long target = 2LL * cus;
     long long want = ((long long)S_max * streams + target - 1) / target;
     chunk = round_up(want, kChunkQuantum);
-    if (chunk < 256) chunk = 256;
+    if (chunk < 512) chunk = 512;
     if (chunk > 2048) chunk = 2048;
+    const int min_chunk = round_up((S_max + kMaxAutoSplits - 1) / kMaxAutoSplits, kChunkQuantum);
+    if (chunk < min_chunk) chunk = min_chunk;
   }
   if (chunk > full) chunk = full;
   const int ns = (S_max + chunk - 1) / chunk;
@@ -68,9 +75,16 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
   return PARALLAX_OK;
 }
 
+size_t records_bytes(int B, int H_q, int d, int ns) {
+  return (size_t)B * H_q * ns * (size_t)(2 * d + 4) * sizeof(float);
+}
+
+// Partial records, then one 32-bit arrival counter per (b, query head) (an
+// upper bound on the (b, KV head, head group) streams), rounded to 16 bytes.
 size_t workspace_bytes_for(int B, int H_q, int d, int ns) {
   if (B <= 0 || H_q <= 0 || d <= 0 || ns <= 1) return 0;
-  return (size_t)B * H_q * ns * (size_t)(2 * d + 4) * sizeof(float);
+  const size_t ctr = ((size_t)B * H_q * sizeof(uint32_t) + 15) / 16 * 16;
+  return records_bytes(B, H_q, d, ns) + ctr;
 }
 
 struct Checked {
@@ -110,8 +124,11 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
     if (!aligned16(ws)) return PARALLAX_ERR_MISALIGNED;
   }
   c->ws_need = need;
-  c->a = parallax::DecodeArgs{q, rho, k, v, seq_lens, out, ws, B, H_q, H_kv, G, d, S_max,
-                              ns, chunk, scale, dtype == PARALLAX_F32};
+  void* counters = nullptr;
+  if (need > 0 && need_out)
+    counters = static_cast<char*>(ws) + records_bytes(B, H_q, d, ns);
+  c->a = parallax::DecodeArgs{q, rho, k, v, seq_lens, out, ws, counters, B, H_q, H_kv, G,
+                              d, S_max, ns, chunk, scale, dtype == PARALLAX_F32};
   return PARALLAX_OK;
 }
 
@@ -215,11 +232,8 @@ parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_
                                         H_kv, d, S_max, scale, dtype, num_splits, workspace,
                                         workspace_bytes, &c);
     if (st != PARALLAX_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = parallax::launch_decode_partial(c.a, s);
-    if (e != hipSuccess) return PARALLAX_ERR_HIP;
-    if (c.a.num_splits > 1) e = parallax::launch_decode_combine(c.a, s);
-    return hip_status(e);
+    // one launch: with several splits the last workgroup of each stream merges
+    return hip_status(parallax::launch_decode_partial(c.a, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return PARALLAX_ERR_HIP;
   }

@@ -102,12 +102,80 @@ __device__ __forceinline__ uint32_t load_probe_words(const T* p, int n, uint32_t
   return 0;
 }
 
+// Merges the partial records of splits 0..nsv-1 of one (b, h_q) at the two
+// dimensions 2 p and 2 p + 1 (records are REC = 2D+4 floats apart: m, l, Bs,
+// c, A[D], C[D]) and returns the two finalised outputs. Online over the
+// splits (the running max only grows; the probe reference is split 0's), with
+// the loads of 8 splits issued before any of them is used. kCoherent reads
+// with agent-scope atomic loads (records written by other workgroups in the
+// same launch, possibly through another XCD's L2).
+template <int D, bool kCoherent = false>
+__device__ __forceinline__ f32x2 merge_records(const float* __restrict__ base, int nsv, int p) {
+  constexpr int REC = 2 * D + 4;
+  constexpr int NB = 8;
+  auto get = [](const float* q) {
+    if constexpr (kCoherent)
+      return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      return *q;
+  };
+  auto get2 = [](const float* q) {
+    if constexpr (kCoherent) {
+      const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(q), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      return __builtin_bit_cast(f32x2, u);
+    } else {
+      return *reinterpret_cast<const f32x2*>(q);
+    }
+  };
+  if (nsv <= 0) return f32x2{0.f, 0.f};
+  const float c0 = get(base + 3);
+  float M = -INFINITY, l = 0.f, bs = 0.f;
+  f32x2 A = {0.f, 0.f}, C = {0.f, 0.f};
+  for (int s0 = 0; s0 < nsv; s0 += NB) {
+    float ms[NB], lw[NB], bw[NB], cw[NB];
+    f32x2 Aw[NB], Cw[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float* rec = base + (size_t)min(s0 + i, nsv - 1) * REC;
+      ms[i] = get(rec + 0);
+      lw[i] = get(rec + 1);
+      bw[i] = get(rec + 2);
+      cw[i] = get(rec + 3);
+      Aw[i] = get2(rec + 4 + 2 * p);
+      Cw[i] = get2(rec + 4 + D + 2 * p);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (s0 + i < nsv) {
+        if (ms[i] > M) {
+          const float f = exp2f(M - ms[i]);
+          l *= f;
+          bs *= f;
+          A *= f;
+          C *= f;
+          M = ms[i];
+        }
+        const float al = exp2f(ms[i] - M);
+        const float sh = cw[i] - c0;
+        l += al * lw[i];
+        bs += al * (bw[i] + sh * lw[i]);
+        A += al * Aw[i];
+        C += al * (Cw[i] + sh * Aw[i]);
+      }
+    }
+  }
+  if (!(l > 0.f)) return f32x2{0.f, 0.f};
+  const float g = 1.f + bs / l;
+  return (A * g - C) / l;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ rho, const T* __restrict__ kc,
     const T* __restrict__ vc, const int32_t* __restrict__ seq_lens, float* __restrict__ out,
-    float* __restrict__ ws, int H_q, int H_kv, int G, int S_max, int chunk, int num_splits,
-    float scale_log2) {
+    float* __restrict__ ws, unsigned* __restrict__ counters, int H_q, int H_kv, int G, int S_max,
+    int chunk, int num_splits, float scale_log2) {
   using P = Dec<T, D>;
   __shared__ float lds_state[kWaves][4][4];          // m, l, bs, cref per head
   __shared__ float lds_vec[kWaves][2][4][D];         // A, C per head
@@ -123,7 +191,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int n = min(max(seq_lens[b], 0), S_max);
   const int j0 = split * chunk;
   const bool direct = (num_splits == 1);
-  if (j0 >= n && !direct) return;                    // empty split: combine skips it
+  const bool fused = counters != nullptr;            // last workgroup merges the splits
+  if (j0 >= n && !direct) {                          // empty split: the merge skips it
+    if (fused && n == 0 && split == 0) {             // no workgroup holds a key
+      for (int idx = threadIdx.x; idx < Gw * D; idx += 256)
+        out[((size_t)b * H_q + h0) * D + idx] = 0.f;
+    }
+    return;
+  }
   const int j1 = min(j0 + chunk, n);
 
   const int tid = threadIdx.x;
@@ -163,20 +238,24 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   float cref = 0.f;     // probe reference for head hq
   bool first = true;
 
-  for (int blk = j0 + kBlockKeys * wave; blk < j1; blk += kBlockKeys * kWaves) {
-    // ---- loads: K pieces for the score MFMA, V rows for the value MFMA
-    Words<P::KW> kw[2][P::KSTEPS];
+  // K pieces for the score MFMA and V rows for the value MFMA of one block.
+  auto load_block = [&](int blk, Words<P::KW> (&kw)[2][P::KSTEPS], Words<P::VW> (&vw)[8]) {
 #pragma unroll
     for (int T2 = 0; T2 < 2; ++T2)
 #pragma unroll
       for (int kk = 0; kk < P::KSTEPS; ++kk)
         kw[T2][kk] = buffer_load<P::KW>(
             krs, (uint32_t)(blk + 16 * T2 + c) * P::ROWB + (32 * kk + 8 * g) * P::ESZ);
-    Words<P::VW> vw[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       vw[e] = buffer_load<P::VW>(
           vrs, (uint32_t)(blk + 16 * (e >> 2) + 4 * g + (e & 3)) * P::ROWB + P::DPL * c * P::ESZ);
+  };
+
+  for (int blk = j0 + kBlockKeys * wave; blk < j1; blk += kBlockKeys * kWaves) {
+    Words<P::KW> kw[2][P::KSTEPS];
+    Words<P::VW> vw[8];
+    load_block(blk, kw, vw);
 
     // ---- scores: lane (g, c) gets probe column c for keys 16 T2 + 4 g + i
     f32x4 sc[2];
@@ -291,7 +370,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
   __syncthreads();
 
-  // ---- merge the 4 waves; finalise (one split) or write the partial record
+  // ---- merge the 4 waves; finalise (one split) or write the partial record.
+  // With the fused merge the records are written with agent-scope atomic
+  // stores, which go to the device-coherent level instead of staying in this
+  // XCD's L2, so the merging workgroup (on any XCD) reads them without any
+  // cache-wide write-back or invalidate.
+  auto put = [&](float* p, float v) {
+    if (fused)
+      __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = v;
+  };
   for (int idx = tid; idx < Gw * D; idx += 256) {
     const int h = idx / D;
     const int dim = idx % D;
@@ -325,48 +414,59 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     } else {
       float* rec = ws + (((size_t)b * H_q + h0 + h) * num_splits + split) * P::REC;
       if (dim == 0) {
-        rec[0] = M;
-        rec[1] = l;
-        rec[2] = bs;
-        rec[3] = c0;
+        put(rec + 0, M);
+        put(rec + 1, l);
+        put(rec + 2, bs);
+        put(rec + 3, c0);
       }
-      rec[4 + dim] = A;
-      rec[4 + D + dim] = C;
+      put(rec + 4 + dim, A);
+      put(rec + 4 + D + dim, C);
     }
+  }
+  if (direct || !fused) return;
+
+  // ---- fused merge: the workgroup that finishes last for this (b, KV head,
+  // head group) merges every split's record. Each thread waits until its own
+  // coherent record stores have completed before the workgroup barrier, so
+  // they are performed before thread 0's arrival increment; the last arrival
+  // reads the records with agent-scope atomic loads (also at the coherent
+  // level) and returns the counter to zero.
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    unsigned* ctr = counters + ((size_t)b * H_kv + hk) * ngroups + hgrp;
+    const unsigned nsv = (unsigned)((n + chunk - 1) / chunk);
+    const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev + 1 == nsv);
+    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const int nsv = (n + chunk - 1) / chunk;
+  for (int idx = tid; idx < Gw * D / 2; idx += 256) {  // (head, pair of dims)
+    const int h = idx / (D / 2);
+    const int p = idx % (D / 2);
+    const float* base = ws + ((size_t)b * H_q + h0 + h) * num_splits * P::REC;
+    *reinterpret_cast<f32x2*>(out + ((size_t)b * H_q + h0 + h) * D + 2 * p) =
+        merge_records<D, true>(base, nsv, p);
   }
 }
 
-// One workgroup of D threads per (b, h_q): merges the partial records of the
-// splits that hold keys and writes out[b, h_q, :].
+// One workgroup of D/2 threads per (b, h_q): merges the partial records of
+// the splits that hold keys and writes out[b, h_q, :].
 template <int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __restrict__ seq_lens,
+__global__ __launch_bounds__(64) void decode_combine_kernel(const int32_t* __restrict__ seq_lens,
                                                              const float* __restrict__ ws,
                                                              float* __restrict__ out, int H_q,
                                                              int S_max, int chunk, int num_splits) {
   constexpr int REC = 2 * D + 4;
   const int bh = blockIdx.x;
   const int b = bh / H_q;
-  const int dim = threadIdx.x;
   const int n = min(max(seq_lens[b], 0), S_max);
   const int nsv = min(num_splits, (n + chunk - 1) / chunk);
-  const float* base = ws + (size_t)bh * num_splits * REC;
-  float M = -INFINITY;
-  for (int s = 0; s < nsv; ++s) M = fmaxf(M, base[(size_t)s * REC]);
-  const float c0 = nsv > 0 ? base[3] : 0.f;
-  float l = 0.f, bs = 0.f, A = 0.f, C = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < nsv; ++s) {
-    const float* rec = base + (size_t)s * REC;
-    const float al = exp2f(rec[0] - M);
-    const float lw = rec[1];
-    const float sh = rec[3] - c0;
-    const float Aw = rec[4 + dim];
-    l += al * lw;
-    bs += al * (rec[2] + sh * lw);
-    A += al * Aw;
-    C += al * (rec[4 + D + dim] + sh * Aw);
-  }
-  out[(size_t)bh * D + dim] = l > 0.f ? (A * (1.f + bs / l) - C) / l : 0.f;
+  *reinterpret_cast<f32x2*>(out + (size_t)bh * D + 2 * threadIdx.x) =
+      merge_records<D>(ws + (size_t)bh * num_splits * REC, nsv, threadIdx.x);
 }
 
 template <typename T, int D>
@@ -376,8 +476,8 @@ hipError_t launch_partial_t(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_partial_kernel<T, D>), grid, dim3(256), 0, st,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.rho),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.seq_lens, a.out,
-                     static_cast<float*>(a.ws), a.H_q, a.H_kv, a.G, a.S_max, a.chunk,
-                     a.num_splits, a.scale * kLog2e);
+                     static_cast<float*>(a.ws), static_cast<unsigned*>(a.counters), a.H_q,
+                     a.H_kv, a.G, a.S_max, a.chunk, a.num_splits, a.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -393,11 +493,11 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.B * a.H_q);
   if (a.d == 64) {
-    hipLaunchKernelGGL((decode_combine_kernel<64>), grid, dim3(64), 0, st, a.seq_lens,
+    hipLaunchKernelGGL((decode_combine_kernel<64>), grid, dim3(32), 0, st, a.seq_lens,
                        static_cast<const float*>(a.ws), a.out, a.H_q, a.S_max, a.chunk,
                        a.num_splits);
   } else {
-    hipLaunchKernelGGL((decode_combine_kernel<128>), grid, dim3(128), 0, st, a.seq_lens,
+    hipLaunchKernelGGL((decode_combine_kernel<128>), grid, dim3(64), 0, st, a.seq_lens,
                        static_cast<const float*>(a.ws), a.out, a.H_q, a.S_max, a.chunk,
                        a.num_splits);
   }

@@ -13,7 +13,8 @@ struct DecodeArgs {
   const void* v;
   const int32_t* seq_lens;
   float* out;
-  void* ws;
+  void* ws;        // partial records [B, H_q, num_splits, 2d + 4] fp32
+  void* counters;  // arrival counters (fused merge), or null for the two-phase form
   int B, H_q, H_kv, G, d, S_max;
   int num_splits, chunk;
   float scale;

@@ -78,7 +78,9 @@ def test_plan_bad_shapes(L):
 
 
 def test_workspace_size(L):
-    assert pa.decode_workspace_size(8, 16, 128, 16) == 8 * 16 * 16 * 260 * 4
+    # records, then one 32-bit arrival counter per (b, h_q), rounded to 16 bytes
+    assert pa.decode_workspace_size(8, 16, 128, 16) == 8 * 16 * 16 * 260 * 4 + 8 * 16 * 4
+    assert pa.decode_workspace_size(1, 3, 64, 2) == 1 * 3 * 2 * 132 * 4 + 16
     assert pa.decode_workspace_size(8, 16, 128, 1) == 0
     assert pa.decode_workspace_size(0, 16, 128, 4) == 0
 

@@ -184,3 +184,21 @@ def test_workload4_full_sampled():
     w = WORKLOADS[4]
     heads = [(0, 0), (0, 5), (0, 18), (0, 31)]
     _sampled(w, heads)
+
+
+def test_fused_workspace_reuse_counters_return_to_zero():
+    """One zeroed workspace serves successive fused calls with different lengths."""
+    w = SMALL2
+    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.S_max, 6)
+    nbytes = pa.decode_workspace_size(w.B, w.H_q, w.d, ns)
+    ws = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    rec_words = w.B * w.H_q * ns * (2 * w.d + 4)
+    for lens in ([700, 333, 97], [5, 700, 0], [129, 128, 700], [0, 0, 0]):
+        cpu = make_decode_inputs(w, seq_lens=lens)
+        dev = to_dev(cpu)
+        out = pa.decode(dev["q"], dev["rho"], dev["k_cache"], dev["v_cache"], dev["seq_lens"],
+                        dev["scale"], num_splits=6, workspace=ws)
+        torch.cuda.synchronize()
+        assert rel_err(out.cpu().numpy(), oracle_all(cpu)) < TOL
+        ctr = ws[rec_words:].view(torch.int32)
+        assert int(ctr.abs().sum()) == 0
