@@ -226,7 +226,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", choices=["all", "main"], default="all")
+    ap.add_argument("--workloads", choices=["all", "main", "prefill"], default="all",
+                    help="all: every workload; main: the GQA decode line only; "
+                         "prefill: the causal prefill only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -253,6 +255,12 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    if args.workloads == "prefill":
+        log("workload causal-prefill")
+        res = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 3)
+        print(json.dumps({"workload": WORKLOADS[5].name, **res}), flush=True)
+        return
 
     w = WORKLOADS[2]
     log(f"main workload {w.name}")

@@ -16,9 +16,9 @@
 // accumulated products.
 //
 // Tiling. A workgroup of 4 waves owns 128 query rows of one (b, h); each wave
-// owns 32 rows. Key blocks of 32 keys are staged in LDS (rows padded by 16
-// bytes against bank conflicts) and shared by the 4 waves; the next block's
-// global loads are in flight while the current block is contracted. Per wave
+// owns 32 rows. Key blocks of 32 keys are staged in double-buffered LDS (rows
+// padded by 16 bytes against bank conflicts) and shared by the 4 waves; a
+// block's global loads are issued two blocks before it is needed. Per wave
 // and key block, v_mfma_f32_32x32x16_bf16 computes the transposed scores
 // S^T = K Q^T and R^T = K rho^T, so lane l holds query row l % 32 for keys
 // 8p + 4 (l / 32) + i (p, i = 0..3): the row max and sums are lane-local plus
@@ -62,8 +62,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, float* __restrict__ out,
     int H_q, int H_kv, int G, int T, int S_max, float scale_log2) {
   using P = Pre<D>;
-  __shared__ __attribute__((aligned(16))) char kv_lds[2][kKeys * P::LSTR];  // K, V tiles
+  __shared__ __attribute__((aligned(16))) char kv_lds[2][2][kKeys * P::LSTR];  // [buffer][K, V]
   __shared__ float row_lds[4][2][32];  // per wave: two per-row scalars
+  static_assert(2 * 2 * kKeys * Pre<D>::LSTR + sizeof(float) * 256 <= 65536, "LDS budget");
 
   const int nrb = (T + kRows - 1) / kRows;
   const int rb = nrb - 1 - (int)blockIdx.x;  // late (heavy) row blocks first
@@ -119,29 +120,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int wave_last_key = min(wrow0 + 31, n - 1);
   const int wave_nkb = wave_last_key >= 0 && wrow0 < n ? wave_last_key / kKeys + 1 : 0;
 
-  // tile pieces of this thread: piece p -> (tile K/V, row, 16-byte column)
-  i32x4 stage[P::PPT];
-  auto load_tile = [&](int kb) {
+  // tile pieces of this thread (16 bytes each); two register stages so that a
+  // block's loads are issued two blocks ahead
+  i32x4 stage[2][P::PPT];
+  // Pieces 0 .. PPT/2-1 of a thread are K, the rest V (a compile-time split,
+  // so the buffer descriptor stays wave-uniform).
+  auto load_tile = [&](int kb, i32x4 (&dst)[P::PPT]) {
 #pragma unroll
     for (int i = 0; i < P::PPT; ++i) {
-      const int p = tid + 256 * i;
-      const int which = p / P::PIECES;
-      const int idx = p % P::PIECES;
+      const int idx = tid + 256 * (i % (P::PPT / 2));
       const int r = idx / (P::ROWB / 16);
       const int c16 = idx % (P::ROWB / 16);
       const uint32_t off = (uint32_t)(kb * kKeys + r) * P::ROWB + c16 * 16;
-      stage[i] = __builtin_amdgcn_raw_buffer_load_b128(which ? vrs : krs, off, 0, 0);
+      dst[i] = __builtin_amdgcn_raw_buffer_load_b128(i < P::PPT / 2 ? krs : vrs, off, 0, 0);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf, const i32x4 (&src)[P::PPT]) {
 #pragma unroll
     for (int i = 0; i < P::PPT; ++i) {
-      const int p = tid + 256 * i;
-      const int which = p / P::PIECES;
-      const int idx = p % P::PIECES;
+      const int idx = tid + 256 * (i % (P::PPT / 2));
       const int r = idx / (P::ROWB / 16);
       const int c16 = idx % (P::ROWB / 16);
-      *reinterpret_cast<i32x4*>(&kv_lds[which][r * P::LSTR + c16 * 16]) = stage[i];
+      *reinterpret_cast<i32x4*>(&kv_lds[buf][i < P::PPT / 2 ? 0 : 1][r * P::LSTR + c16 * 16]) = src[i];
     }
   };
 
@@ -156,18 +156,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   float bsum = 0.f;     // this lane's part of Bs
   float cref = 0.f;     // rho_t . k_0
 
-  load_tile(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // previous block's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (kb + 1 < nkb) load_tile(kb + 1);
-    if (kb >= wave_nkb) continue;  // keys past this wave's last row
-
-    // ---- transposed scores: lane holds row my_row, keys 8 pp + 4 half + i
+  // Contracts key block kb (LDS buffer buf) into this wave's accumulators.
+  auto contract = [&](int kb, int buf) {
+    // ---- transposed scores: lane holds row my_row, keys 8 (r / 4) + 4 half + r % 4
     f32x16_t sacc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     f32x16_t racc = sacc;
-    const char* krow = &kv_lds[0][col * P::LSTR + 16 * half];
+    const char* krow = &kv_lds[buf][0][col * P::LSTR + 16 * half];
 #pragma unroll
     for (int kk = 0; kk < P::KST; ++kk) {
       const i32x4 kw = *reinterpret_cast<const i32x4*>(krow + 32 * kk);
@@ -179,16 +173,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
     float x[16];
     float mx = -INFINITY;
+    if (kb * kKeys + kKeys - 1 > wrow0) {  // diagonal block: causal mask
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb * kKeys + 8 * (r >> 2) + 4 * half + (r & 3);
-      const float s = key <= my_row ? sacc[r] * scale_log2 : -INFINITY;
-      x[r] = s;
-      mx = fmaxf(mx, s);
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * kKeys + 8 * (r >> 2) + 4 * half + (r & 3);
+        x[r] = key <= my_row ? sacc[r] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = sacc[r] * scale_log2;
+        mx = fmaxf(mx, x[r]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // rows past the sequence have no key in range only if my_row >= n; they
-    // still see key 0..my_row (zero operands), so mx is finite for every row
 
     const bool need = mx > m + kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -212,27 +211,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- weights and their hi/lo bf16 split; A operands of the value MFMAs
-    uint32_t phw[8], plw[8], qhw[8], qlw[8];  // e hi/lo, e*r hi/lo (2 per word)
+    // ---- weights e and e (r - c), each as packed bf16 high part and the
+    // bf16 rounding of the remainder: the A operands of the value MFMAs
+    uint32_t phw[8], plw[8], qhw[8], qlw[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      float e2[2], er2[2], eh[2], erh[2];
-#pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const int r = 2 * u + z;
-        const float e = __builtin_amdgcn_exp2f(x[r] - m);
-        const float er = e * (racc[r] - cref);
-        lsum += e;
-        bsum += er;
-        e2[z] = e;
-        er2[z] = er;
-        eh[z] = bf16_round(e);
-        erh[z] = bf16_round(er);
-      }
-      phw[u] = pack_bf16(e2[0], e2[1]);
-      qhw[u] = pack_bf16(er2[0], er2[1]);
-      plw[u] = pack_bf16(e2[0] - eh[0], e2[1] - eh[1]);
-      qlw[u] = pack_bf16(er2[0] - erh[0], er2[1] - erh[1]);
+      const float e0 = __builtin_amdgcn_exp2f(x[2 * u] - m);
+      const float e1 = __builtin_amdgcn_exp2f(x[2 * u + 1] - m);
+      const float f0 = e0 * (racc[2 * u] - cref);
+      const float f1 = e1 * (racc[2 * u + 1] - cref);
+      lsum += e0 + e1;
+      bsum += f0 + f1;
+      const uint32_t ph = pack_bf16(e0, e1);
+      const uint32_t qh = pack_bf16(f0, f1);
+      phw[u] = ph;
+      qhw[u] = qh;
+      plw[u] = pack_bf16(e0 - bf16_lo(ph), e1 - bf16_hi(ph));
+      qlw[u] = pack_bf16(f0 - bf16_lo(qh), f1 - bf16_hi(qh));
     }
 
     // ---- value MFMAs over the two 16-key halves of the block
@@ -243,11 +238,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       const bf16x8 a_qh = as_bf16x8(qhw[4 * uu], qhw[4 * uu + 1], qhw[4 * uu + 2], qhw[4 * uu + 3]);
       const bf16x8 a_ql = as_bf16x8(qlw[4 * uu], qlw[4 * uu + 1], qlw[4 * uu + 2], qlw[4 * uu + 3]);
       // V rows of key slots e = 0..7: keys 16 uu + (e < 4 ? 4 half + e : 8 + 4 half + e - 4)
-      uint32_t vw[8][P::NT / 2];
+      uint32_t vw[8][(P::NT + 1) / 2];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = 16 * uu + (e < 4 ? 4 * half + e : 8 + 4 * half + (e - 4));
-        const char* vp = &kv_lds[1][key * P::LSTR + col * (2 * P::NT)];
+        const char* vp = &kv_lds[buf][1][key * P::LSTR + col * (2 * P::NT)];
         if constexpr (P::NT == 4) {
           const i32x2 w = *reinterpret_cast<const i32x2*>(vp);
           vw[e][0] = (uint32_t)w[0];
@@ -268,6 +263,31 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         accC[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ql, vop, accC[j], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline, one barrier per block: block kb is contracted from LDS buffer
+  // kb % 2 while block kb + 1 goes from registers into the other buffer and
+  // block kb + 3 is loaded from HBM into the registers just freed (two
+  // register stages, so each load has two blocks of contraction to land).
+  // One pipeline step for block kb, with `next` holding block kb + 1's pieces
+  // (register stage (kb + 1) % 2, named statically by the 2-way unrolled loop).
+  // Loads and stores run unconditionally: loads past the sequence are
+  // range-checked to zeros without touching memory, and uniform control flow
+  // lets the compiler wait only for the older register stage.
+  auto step = [&](int kb, int buf, i32x4 (&next)[P::PPT]) {
+    if (kb < wave_nkb) contract(kb, buf);
+    store_tile(buf ^ 1, next);
+    load_tile(kb + 3, next);
+    __syncthreads();
+  };
+  load_tile(0, stage[0]);
+  load_tile(1, stage[1]);
+  store_tile(0, stage[0]);
+  load_tile(2, stage[0]);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, 0, stage[1]);
+    step(kb + 1, 1, stage[0]);
   }
 
   // ---- finalise: per-row l and Bs to the output layout through LDS
