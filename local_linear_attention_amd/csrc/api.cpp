@@ -253,7 +253,7 @@ parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k
     if (((long long)S_max + 256) * d * 2 >= (1LL << 31) ||
         ((long long)T + 256) * d * 2 >= (1LL << 31))
       return PARALLAX_ERR_UNSUPPORTED;
-    if ((long long)B * H_q > 65535LL * 65535LL) return PARALLAX_ERR_UNSUPPORTED;
+    if (B > 65535 || H_q > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y, z limits
     if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;
     if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
