@@ -26,7 +26,10 @@
 // query heads, key range of `chunk` keys). Each wave takes every 4th block
 // of 32 keys. Per block a lane loads its K and V pieces straight from HBM into
 // registers with range-checked buffer loads (rows at or past the sequence
-// length come back as zeros, so padding is never read), and two MFMA
+// length come back as zeros, so padding is never read). V rows, read in whole
+// 256-byte rows per instruction, carry the non-temporal streaming hint; K is
+// read as 64-byte pieces of 16 rows per instruction, whose two halves of each
+// 128-byte line must meet in L2, so K keeps the default policy. Two MFMA
 // contractions do the arithmetic:
 //   scores:  [32 keys x d] x [d x 16 probe columns] with v_mfma_f32_16x16x32_bf16,
 //            probe column 4h+t holds q_h for t in {0,1} and rho_h for t in {2,3},
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
             krs, (uint32_t)(blk + 16 * T2 + c) * P::ROWB + (32 * kk + 8 * g) * P::ESZ);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      vw[e] = buffer_load<P::VW>(
+      vw[e] = buffer_load<P::VW, kNontemporal>(
           vrs, (uint32_t)(blk + 16 * (e >> 2) + 4 * g + (e & 3)) * P::ROWB + P::DPL * c * P::ESZ);
   };
 

@@ -28,28 +28,32 @@ struct Words {
   uint32_t w[N];
 };
 
-template <int N>
+// Cache-policy operand of a buffer load: 0 = default, kNontemporal = the
+// streaming hint for data read once (CDNA3/4 "nt" bit).
+constexpr int kNontemporal = 2;
+
+template <int N, int AUX = 0>
 __device__ __forceinline__ Words<N> buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   Words<N> out;
   if constexpr (N == 8) {
-    i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+    i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    i32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, AUX);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out.w[i] = (uint32_t)a[i];
       out.w[4 + i] = (uint32_t)b[i];
     }
   } else if constexpr (N == 4) {
-    i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    i32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
 #pragma unroll
     for (int i = 0; i < 4; ++i) out.w[i] = (uint32_t)a[i];
   } else if constexpr (N == 2) {
-    i32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    i32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
     out.w[0] = (uint32_t)a[0];
     out.w[1] = (uint32_t)a[1];
   } else {
     static_assert(N == 1, "unsupported load width");
-    out.w[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    out.w[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
   }
   return out;
 }
