@@ -108,7 +108,8 @@ __device__ __forceinline__ uint32_t load_probe_words(const T* p, int n, uint32_t
 // Merges the partial records of splits 0..nsv-1 of one (b, h_q) at the two
 // dimensions 2 p and 2 p + 1 (records are REC = 2D+4 floats apart: m, l, Bs,
 // c, A[D], C[D]) and returns the two finalised outputs. Online over the
-// splits (the running max only grows; the probe reference is split 0's), with
+// splits (the running max only grows; records with l = 0 hold no key and are
+// skipped; the probe reference is the first non-empty record's), with
 // the loads of 8 splits issued before any of them is used. kCoherent reads
 // with agent-scope atomic loads (records written by other workgroups in the
 // same launch, possibly through another XCD's L2).
@@ -132,7 +133,8 @@ __device__ __forceinline__ f32x2 merge_records(const float* __restrict__ base, i
     }
   };
   if (nsv <= 0) return f32x2{0.f, 0.f};
-  const float c0 = get(base + 3);
+  float c0 = 0.f;
+  bool have = false;  // the reference c0 is the first non-empty record's
   float M = -INFINITY, l = 0.f, bs = 0.f;
   f32x2 A = {0.f, 0.f}, C = {0.f, 0.f};
   for (int s0 = 0; s0 < nsv; s0 += NB) {
@@ -150,7 +152,11 @@ __device__ __forceinline__ f32x2 merge_records(const float* __restrict__ base, i
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      if (s0 + i < nsv) {
+      if (s0 + i < nsv && lw[i] > 0.f) {  // a record with l = 0 holds no key
+        if (!have) {
+          c0 = cw[i];
+          have = true;
+        }
         if (ms[i] > M) {
           const float f = exp2f(M - ms[i]);
           l *= f;
