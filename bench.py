@@ -14,7 +14,8 @@ mean step time. A step is a single kernel launch, so a pair of HIP events on
 the launch stream around the timed region, divided by K, gives the kernel's
 average launch duration for the `roofline` object. The other workloads (single-head fp32, ragged batch,
 128K-context split-KV decode, causal prefill) are timed the same way, briefly,
-and reported under "workloads". The `cpu_baseline` leg times the fp64 oracle
+and reported under "workloads", with a chunked prefill (1024 new rows after
+3072 cached tokens). The `cpu_baseline` leg times the fp64 oracle
 on a bounded sample of the same GQA decode workload on the host cores.
 
 One JSON line is printed at the end.
@@ -175,6 +176,45 @@ def bench_prefill(w, steps, warmup, seed=None):
             "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
 
 
+def bench_chunked(w, steps, warmup, seed=None):
+    """Chunked prefill: w.T new rows after w.past cached tokens per sequence."""
+    import torch
+
+    import local_linear_attention_amd as pa
+    from workloads import make_chunk_inputs
+
+    dev = torch.device("cuda:0")
+    inp = make_chunk_inputs(w, seed=seed, device=dev)
+    out = torch.empty((w.B, w.H_q, w.T, w.d), dtype=torch.float32, device=dev)
+    L = pa.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = (inp["q"].data_ptr(), inp["rho"].data_ptr(), inp["k_cache"].data_ptr(),
+            inp["v_cache"].data_ptr(), inp["past_lens"].data_ptr(), inp["chunk_lens"].data_ptr(),
+            out.data_ptr(), w.B, w.H_q, w.H_kv, w.d, w.T, inp["k_cache"].shape[2],
+            float(inp["scale"]), 0, stream)
+    for _ in range(warmup):
+        if L.parallax_prefill_chunked(*args) != 0:
+            raise RuntimeError("chunked prefill failed")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        L.parallax_prefill_chunked(*args)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = ev0.elapsed_time(ev1) / steps / 1e3
+    # row t sees past + t + 1 keys: 4 contractions of 2 d flops per (row, key)
+    pairs = w.T * w.past + w.T * (w.T + 1) / 2
+    flops = 8.0 * w.d * pairs * w.B * w.H_q
+    return {"us_per_step": (t1 - t0) / steps * 1e6, "kernel_us": kern * 1e6,
+            "algorithmic_tflop": flops / 1e12, "tflops": flops / kern / 1e12,
+            "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "shape": dict(B=w.B, T=w.T, past=w.past, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
+
+
 def cpu_baseline(runner, budget_s=15.0):
     """Times the fp64 oracle on a bounded sample of the GQA decode workload."""
     import numpy as np
@@ -241,7 +281,7 @@ def main():
 
     import torch
 
-    from workloads import WORKLOADS
+    from workloads import CHUNK_WORKLOAD, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -318,10 +358,9 @@ def main():
             del r
             torch.cuda.empty_cache()
         log("workload causal-prefill")
-        try:
-            workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 3)
-        except RuntimeError as e:
-            workloads[WORKLOADS[5].name] = {"error": str(e)}
+        workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 3)
+        log("workload chunked-prefill")
+        workloads[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 3)
     result["workloads"] = workloads
 
     if not args.no_cpu_baseline:

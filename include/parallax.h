@@ -166,6 +166,30 @@ parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k
                                    int H_q, int H_kv, int d, int T, int S_max, float scale,
                                    parallax_dtype_t dtype, void* stream);
 
+/*
+ * Chunked causal prefill against an existing cache (also multi-token decode):
+ * row t of sequence b sits at position past_lens[b] + t and sees keys
+ * 0 .. past_lens[b] + t of the cache. The cache must already hold the
+ * chunk's own keys and values at positions past_lens[b] .. past_lens[b] +
+ * chunk_lens[b] - 1 (append first, then attend). With every past length 0 this
+ * is parallax_prefill.
+ *   q, rho      [B, H_q, T, d]       dtype (rho is per token)
+ *   k_cache,
+ *   v_cache     [B, H_kv, S_max, d]  dtype, T <= S_max
+ *   past_lens   [B]                  int32 (device), clamped to [0, S_max]
+ *   chunk_lens  [B]                  int32 (device), valid rows of the chunk,
+ *                                    clamped to [0, min(T, S_max - past)];
+ *                                    rows t >= chunk_lens[b] are written as 0
+ *   out         [B, H_q, T, d]       fp32, written in full
+ * Only dtype PARALLAX_BF16 is built. Errors as parallax_prefill, plus
+ * PARALLAX_ERR_NULL_POINTER for a NULL past_lens.
+ */
+parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const void* k_cache,
+                                           const void* v_cache, const int32_t* past_lens,
+                                           const int32_t* chunk_lens, float* out, int B, int H_q,
+                                           int H_kv, int d, int T, int S_max, float scale,
+                                           parallax_dtype_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

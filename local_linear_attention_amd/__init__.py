@@ -9,7 +9,7 @@ Functions mirror the C entry points:
 
 * ``decode_plan``, ``decode_workspace_size``
 * ``decode`` (one shot), ``decode_partial`` + ``decode_combine`` (two phases)
-* ``prefill`` (causal)
+* ``prefill`` (causal), ``prefill_chunked`` (causal against an existing cache)
 """
 
 from __future__ import annotations
@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "ParallaxError", "lib", "library_path", "abi_version", "status_string", "decode_plan",
     "decode_workspace_size", "decode", "decode_partial", "decode_combine", "prefill",
-    "STATUS", "EXPORTED_SYMBOLS",
+    "prefill_chunked", "STATUS", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +42,7 @@ _BF16, _F32 = 0, 1
 EXPORTED_SYMBOLS = (
     "parallax_abi_version", "parallax_status_string", "parallax_decode_plan",
     "parallax_decode_workspace_size", "parallax_decode", "parallax_decode_partial",
-    "parallax_decode_combine", "parallax_prefill",
+    "parallax_decode_combine", "parallax_prefill", "parallax_prefill_chunked",
 )
 
 
@@ -92,6 +92,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.parallax_decode_combine.argtypes = [vp, vp, i, i, i, i, i, i, vp, sz, vp]
     L.parallax_prefill.restype = i
     L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.parallax_prefill_chunked.restype = i
+    L.parallax_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     return L
 
 
@@ -229,4 +231,35 @@ def prefill(q, rho, k, v, seq_lens, scale: float, *, out=None):
             q.data_ptr(), rho.data_ptr(), k.data_ptr(), v.data_ptr(), seq_lens.data_ptr(),
             out.data_ptr(), B, H_q, H_kv, d, T, S_max, float(scale), _dtype_code(q),
             _stream_ptr(q.device)), "parallax_prefill")
+    return out
+
+
+def prefill_chunked(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: float, *, out=None):
+    """Chunked causal prefill: row t attends keys 0..past_lens[b] + t of the cache.
+
+    The cache must already hold the chunk's keys and values (see
+    parallax_prefill_chunked). Returns out [B, H_q, T, d] fp32.
+    """
+    for name, t in (("q", q), ("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("past_lens", past_lens), ("chunk_lens", chunk_lens)):
+        _dev_tensor(t, name)
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q is [B, H_q, T, d] and k_cache is [B, H_kv, S_max, d]")
+    B, H_q, T, d = q.shape
+    _, H_kv, S_max, _ = k_cache.shape
+    if rho.shape != q.shape or v_cache.shape != k_cache.shape or k_cache.shape[0] != B \
+            or k_cache.shape[3] != d:
+        raise ValueError("inconsistent chunked-prefill shapes")
+    if not (q.dtype == rho.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, rho, k_cache and v_cache must share one dtype")
+    for name, t in (("past_lens", past_lens), ("chunk_lens", chunk_lens)):
+        if t.dtype != torch.int32 or t.shape != (B,):
+            raise ValueError(f"{name} must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_prefill_chunked(
+            q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            past_lens.data_ptr(), chunk_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, T, S_max,
+            float(scale), _dtype_code(q), _stream_ptr(q.device)), "parallax_prefill_chunked")
     return out

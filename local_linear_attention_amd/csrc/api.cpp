@@ -239,28 +239,59 @@ parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+parallax_status_t prefill_common(const void* q, const void* rho, const void* k, const void* v,
+                                 const int32_t* seq_lens, const int32_t* past_lens, float* out,
+                                 int B, int H_q, int H_kv, int d, int T, int S_max, float scale,
+                                 parallax_dtype_t dtype, void* stream) {
+  if (!q || !rho || !k || !v || !seq_lens || !out) return PARALLAX_ERR_NULL_POINTER;
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || T <= 0 || S_max <= 0 || T > S_max ||
+      H_q % H_kv != 0)
+    return PARALLAX_ERR_BAD_SHAPE;
+  if (dtype != PARALLAX_BF16) return PARALLAX_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
+  if (((long long)S_max + 256) * d * 2 >= (1LL << 31) ||
+      ((long long)T + 256) * d * 2 >= (1LL << 31))
+    return PARALLAX_ERR_UNSUPPORTED;
+  if (B > 65535 || H_q > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y, z limits
+  if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;
+  if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(past_lens) & 3u))
+    return PARALLAX_ERR_MISALIGNED;
+  parallax::PrefillArgs a{q,     rho,  k,    v,     seq_lens,  past_lens, out, B,
+                          H_q,   H_kv, H_q / H_kv, d, T, S_max,     scale};
+  return hip_status(parallax::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
 parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k, const void* v,
                                    const int32_t* seq_lens, float* out, int B, int H_q, int H_kv,
                                    int d, int T, int S_max, float scale, parallax_dtype_t dtype,
                                    void* stream) {
   try {
-    if (!q || !rho || !k || !v || !seq_lens || !out) return PARALLAX_ERR_NULL_POINTER;
-    if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || T <= 0 || S_max <= 0 || T > S_max ||
-        H_q % H_kv != 0)
-      return PARALLAX_ERR_BAD_SHAPE;
-    if (dtype != PARALLAX_BF16) return PARALLAX_ERR_UNSUPPORTED;
-    if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
-    if (((long long)S_max + 256) * d * 2 >= (1LL << 31) ||
-        ((long long)T + 256) * d * 2 >= (1LL << 31))
-      return PARALLAX_ERR_UNSUPPORTED;
-    if (B > 65535 || H_q > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y, z limits
-    if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;
-    if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
-      return PARALLAX_ERR_MISALIGNED;
-    parallax::PrefillArgs a{q, rho, k, v, seq_lens, out, B, H_q, H_kv, H_q / H_kv, d, T, S_max,
-                            scale};
-    return hip_status(parallax::launch_prefill(a, static_cast<hipStream_t>(stream)));
+    return prefill_common(q, rho, k, v, seq_lens, nullptr, out, B, H_q, H_kv, d, T, S_max, scale,
+                          dtype, stream);
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const void* k_cache,
+                                           const void* v_cache, const int32_t* past_lens,
+                                           const int32_t* chunk_lens, float* out, int B, int H_q,
+                                           int H_kv, int d, int T, int S_max, float scale,
+                                           parallax_dtype_t dtype, void* stream) {
+  try {
+    if (!past_lens) return PARALLAX_ERR_NULL_POINTER;
+    return prefill_common(q, rho, k_cache, v_cache, chunk_lens, past_lens, out, B, H_q, H_kv, d,
+                          T, S_max, scale, dtype, stream);
   } catch (...) {
     return PARALLAX_ERR_HIP;
   }

@@ -27,6 +27,7 @@ struct PrefillArgs {
   const void* k;
   const void* v;
   const int32_t* seq_lens;
+  const int32_t* past_lens;  // null: no past (plain causal prefill)
   float* out;
   int B, H_q, H_kv, G, d, T, S_max;
   float scale;

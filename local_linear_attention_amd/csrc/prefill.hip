@@ -1,6 +1,8 @@
 // Parallax causal prefill on CDNA4 (gfx950).
 //
-// Row t of sequence b, query head h, sees keys 0..t of KV head h / G
+// Row t of sequence b, query head h, sees keys 0..t of KV head h / G (with a
+// per-sequence past length p, the chunked form: row t sits at position p + t
+// and sees keys 0..p + t of the cache, which already holds the chunk's keys)
 // ("Parallax: Parameterized Local Linear Attention for Language Modeling",
 // paper page, "Abstract": the extra projector rho is query-like, so it is per
 // token here like q; blog "Parallax: Breaking the Boundary Bias with
@@ -61,8 +63,9 @@ struct Pre {
 template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
-    const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens, float* __restrict__ out,
-    int H_q, int H_kv, int G, int T, int S_max, float scale_log2) {
+    const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ past_lens, float* __restrict__ out, int H_q, int H_kv, int G, int T,
+    int S_max, float scale_log2) {
   using P = Pre<D>;
   __shared__ __attribute__((aligned(16))) char kv_lds[2][2][P::TILE];  // [buffer][K, V]
 
@@ -71,7 +74,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int hk = h / G;
-  const int n = min(max(seq_lens[b], 0), T);  // rows t >= n are zero; keys j <= t < n
+  // Row t of this chunk sits at position past + t of the sequence and sees
+  // keys 0 .. past + t of the cache; rows t >= n are zero.
+  const int past = past_lens ? min(max(past_lens[b], 0), S_max) : 0;
+  const int n = min(min(max(seq_lens[b], 0), T), S_max - past);
   const int R0 = rb * kRows;
 
   const int tid = threadIdx.x;
@@ -111,13 +117,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 
   const size_t kvslice = ((size_t)b * H_kv + hk) * (size_t)S_max * D;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + kvslice, (uint32_t)n * P::ROWB);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + kvslice, (uint32_t)n * P::ROWB);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + kvslice, (uint32_t)(past + n) * P::ROWB);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + kvslice, (uint32_t)(past + n) * P::ROWB);
 
   // keys this workgroup needs, and this wave's number of key blocks
-  const int wg_keys = min(R0 + kRows, n);
+  const int wg_keys = past + min(R0 + kRows, n);
   const int nkb = (wg_keys + kKeys - 1) / kKeys;
-  const int wave_nkb = wrow0 < n ? min(wrow0 + 15, n - 1) / kKeys + 1 : 0;
+  const int wave_nkb = wrow0 < n ? (past + min(wrow0 + 15, n - 1)) / kKeys + 1 : 0;
+  const int my_pos = past + my_row;  // last key this lane's row sees
 
   // Tile pieces of this thread (16 bytes each). With PPT >= 2 the first half
   // of a thread's pieces are K and the rest V; with PPT == 1 (d = 64) the
@@ -188,11 +195,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     // reaches past this wave's first row.
     float x[8];
     float mx = -INFINITY;
-    if (kb * kKeys + kKeys - 1 > wrow0) {
+    if (kb * kKeys + kKeys - 1 > past + wrow0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = kb * kKeys + 16 * (e >> 2) + 4 * g + (e & 3);
-        x[e] = key <= my_row ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        x[e] = key <= my_pos ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, x[e]);
       }
     } else {
@@ -341,12 +348,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((prefill_kernel<64>), grid, dim3(kThreads), 0, st,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
                        static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                       a.seq_lens, a.out, a.H_q, a.H_kv, a.G, a.T, a.S_max, a.scale * kLog2e);
+                       a.seq_lens, a.past_lens, a.out, a.H_q, a.H_kv, a.G, a.T, a.S_max,
+                       a.scale * kLog2e);
   } else {
     hipLaunchKernelGGL((prefill_kernel<128>), grid, dim3(kThreads), 0, st,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
                        static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                       a.seq_lens, a.out, a.H_q, a.H_kv, a.G, a.T, a.S_max, a.scale * kLog2e);
+                       a.seq_lens, a.past_lens, a.out, a.H_q, a.H_kv, a.G, a.T, a.S_max,
+                       a.scale * kLog2e);
   }
   return hipGetLastError();
 }

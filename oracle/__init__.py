@@ -38,4 +38,6 @@ from .parallax_oracle import (  # noqa: F401
     oracle_decode_heads,
     oracle_prefill_rows,
     oracle_prefill_full,
+    oracle_chunk_rows,
+    oracle_chunk_full,
 )

@@ -181,3 +181,71 @@ def oracle_prefill_full(q, rho, k, v, seq_lens, scale, pairs=None):
             out[:n] = mu_v - corr
         res[(b, h)] = out
     return res
+
+
+def _chunk_bounds(past_lens, chunk_lens, T, S_max):
+    """Per-sequence (past, n) with the clamping the chunked entry point applies."""
+    past = np.clip(np.asarray(_f64(past_lens), dtype=np.int64), 0, S_max)
+    n = np.minimum(np.clip(np.asarray(_f64(chunk_lens), dtype=np.int64), 0, T), S_max - past)
+    return past, n
+
+
+def oracle_chunk_rows(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale, rows):
+    """Chunked causal prefill, explicit Sigma_KV, for chosen (b, h, t) rows.
+
+    Row t of the chunk sits at position p = past_lens[b] + t of the sequence
+    and sees cache keys 0..p (the cache already holds the chunk's own keys);
+    rows t >= chunk_lens[b] are zero. With past 0 this is the causal prefill.
+    q, rho: [B, H_q, T, d]; k_cache, v_cache: [B, H_kv, S_max, d].
+    Returns {(b, h, t): out}.
+    """
+    T = q.shape[2]
+    S_max = k_cache.shape[2]
+    past, n = _chunk_bounds(past_lens, chunk_lens, T, S_max)
+    G = q.shape[1] // k_cache.shape[1]
+    res = {}
+    for b, h, t in rows:
+        if t >= n[b]:
+            res[(b, h, t)] = np.zeros(v_cache.shape[-1], dtype=np.float64)
+            continue
+        p = int(past[b]) + t
+        K = _f64(k_cache[b, h // G, : p + 1])
+        V = _f64(v_cache[b, h // G, : p + 1])
+        res[(b, h, t)] = parallax_attend(_f64(q[b, h, t]), _f64(rho[b, h, t]), K, V, scale)
+    return res
+
+
+def oracle_chunk_full(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale, pairs=None):
+    """Every row of a chunked causal prefill for chosen (b, h) pairs, fp64.
+
+    Same centred definition as ``oracle_prefill_full`` with the mask shifted
+    by the past length: chunk row t sees keys j <= past + t.
+    Returns {(b, h): out [T, d]}.
+    """
+    B, H_q, T, _ = q.shape
+    S_max = k_cache.shape[2]
+    past, n = _chunk_bounds(past_lens, chunk_lens, T, S_max)
+    G = H_q // k_cache.shape[1]
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H_q)]
+    res = {}
+    for b, h in pairs:
+        out = np.zeros((T, v_cache.shape[-1]), dtype=np.float64)
+        nb, pb = int(n[b]), int(past[b])
+        if nb > 0:
+            nk = pb + nb
+            Q = _f64(q[b, h, :nb])
+            R = _f64(rho[b, h, :nb])
+            K = _f64(k_cache[b, h // G, :nk])
+            V = _f64(v_cache[b, h // G, :nk])
+            S = scale * (Q @ K.T)
+            S[np.arange(nk)[None, :] > (pb + np.arange(nb))[:, None]] = -np.inf
+            W = np.exp(S - S.max(axis=1, keepdims=True))
+            W /= W.sum(axis=1, keepdims=True)
+            mu_v = W @ V
+            mu_k = W @ K
+            Rc = R @ K.T - np.sum(R * mu_k, axis=1, keepdims=True)
+            WR = W * Rc
+            out[:nb] = mu_v - (WR @ V - WR.sum(axis=1, keepdims=True) * mu_v)
+        res[(b, h)] = out
+    return res

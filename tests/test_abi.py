@@ -38,7 +38,7 @@ def header_functions():
 
 def test_header_symbols_exported(L):
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert set(names) == set(pa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -154,3 +154,18 @@ def test_python_binding_rejects_cpu_tensors():
     t = torch.zeros(1, 1, 64)
     with pytest.raises(ValueError):
         pa.decode(t, t, t[None], t[None], torch.ones(1, dtype=torch.int32), 1.0)
+
+
+def test_prefill_chunked_argument_errors(L):
+    f = L.parallax_prefill_chunked
+
+    def call(past=P, lens=P, q=P, out=P, T=256, S=512, dtype=BF16, Hq=4, Hkv=2):
+        return f(q, P, P, P, past, lens, out, 2, Hq, Hkv, 128, T, S, 1.0, dtype, None)
+
+    assert call(past=0) == NULLP
+    assert call(lens=0) == NULLP
+    assert call(T=600, S=512) == SHAPE
+    assert call(Hq=5) == SHAPE
+    assert call(dtype=F32) == UNSUP
+    assert call(past=P + 2) == MISAL
+    assert call(q=P + 8) == MISAL

@@ -494,3 +494,95 @@ def test_gqa_mutant_is_caught():
 
 def test_causal_mutant_is_caught():
     assert not (pin_prefill_sdpa(_m_causal_prefill) and pin_prefill_brute(_m_causal_prefill))
+
+
+# ------------------------------------------------------------ chunked prefill
+
+
+def _chunk_case(seed, B=2, Hq=4, Hkv=2, S=40, T=12, d=8):
+    rng = _rng(seed)
+    q_full = rng.standard_normal((B, Hq, S, d))
+    rho_full = rng.standard_normal((B, Hq, S, d)) * 0.2
+    k = rng.standard_normal((B, Hkv, S, d))
+    v = rng.standard_normal((B, Hkv, S, d))
+    return q_full, rho_full, k, v
+
+
+def pin_chunk_equals_prefill(chunk_rows, seed=20):
+    """A chunk at offset p reproduces rows p.. of the (pinned) full causal prefill."""
+    q_full, rho_full, k, v = _chunk_case(seed)
+    S, T = q_full.shape[2], 12
+    past = np.array([17, 5], dtype=np.int32)
+    lens = np.array([T, 9], dtype=np.int32)
+    qc = np.stack([q_full[b, :, past[b]:past[b] + T] for b in range(2)])
+    rc = np.stack([rho_full[b, :, past[b]:past[b] + T] for b in range(2)])
+    rows = [(b, h, t) for b in range(2) for h in range(4) for t in range(T)]
+    got = chunk_rows(qc, rc, k, v, past, lens, 0.7, rows)
+    ref = oracle.oracle_prefill_rows(q_full, rho_full, k, v, np.array([S, S]), 0.7,
+                                     [(b, h, past[b] + t) for b, h, t in rows])
+    for (b, h, t) in rows:
+        want = np.zeros(8) if t >= lens[b] else ref[(b, h, past[b] + t)]
+        if not np.allclose(got[(b, h, t)], want, rtol=1e-12, atol=1e-12):
+            return False
+    return True
+
+
+def pin_chunk_sdpa(chunk_full, seed=21):
+    """rho = 0: torch SDPA with the shifted causal mask (GQA)."""
+    q_full, rho_full, k, v = _chunk_case(seed)
+    T, past = 12, np.array([20, 3], dtype=np.int32)
+    qc = q_full[:, :, :T]
+    got = chunk_full(qc, np.zeros_like(qc), k, v, past, np.array([T, T], dtype=np.int32), 0.5)
+    for b in range(2):
+        nk = past[b] + T
+        mask = torch.tensor(np.arange(nk)[None, :] <= (past[b] + np.arange(T))[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(qc[b])[None], torch.tensor(k[b, :, :nk])[None],
+            torch.tensor(v[b, :, :nk])[None], attn_mask=mask, scale=0.5,
+            enable_gqa=True)[0].numpy()
+        for h in range(4):
+            if not np.allclose(got[(b, h)], ref[h], rtol=1e-12, atol=1e-12):
+                return False
+    return True
+
+
+def test_pin_chunk_equals_full_prefill():
+    assert pin_chunk_equals_prefill(oracle.oracle_chunk_rows)
+
+
+def test_pin_chunk_sdpa_shifted_mask():
+    assert pin_chunk_sdpa(oracle.oracle_chunk_full)
+
+
+def test_chunk_full_matches_rows_and_brute():
+    q_full, rho_full, k, v = _chunk_case(22, S=30, T=10, d=4)
+    qc, rc = q_full[:, :, :10], rho_full[:, :, :10]
+    past = np.array([15, 0], dtype=np.int32)
+    lens = np.array([10, 7], dtype=np.int32)
+    full = oracle.oracle_chunk_full(qc, rc, k, v, past, lens, 0.9)
+    rows = [(b, h, t) for b in range(2) for h in range(4) for t in range(10)]
+    ex = oracle.oracle_chunk_rows(qc, rc, k, v, past, lens, 0.9, rows)
+    for (b, h, t), o in ex.items():
+        np.testing.assert_allclose(full[(b, h)][t], o, rtol=1e-12, atol=1e-12)
+        if t < lens[b]:
+            p = past[b] + t
+            ref = brute_force(qc[b, h, t].tolist(), rc[b, h, t].tolist(),
+                              k[b, h // 2, :p + 1].tolist(), v[b, h // 2, :p + 1].tolist(), 0.9)
+            np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-11)
+
+
+def test_chunk_with_no_past_is_prefill():
+    q, rho, k, v, lens = _prefill_case(23)
+    a = oracle.oracle_chunk_full(q, rho, k, v, np.zeros(2, dtype=np.int32), lens, 0.6)
+    b = oracle.oracle_prefill_full(q, rho, k, v, lens, 0.6)
+    for key in a:
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-13, atol=1e-13)
+
+
+def _m_chunk_offset(q, rho, k, v, past, lens, scale, rows):
+    # off by one: row t sees keys 0..past + t - 1
+    return oracle.oracle_chunk_rows(q, rho, k, v, np.asarray(past) - 1, lens, scale, rows)
+
+
+def test_chunk_offset_mutant_is_caught():
+    assert not pin_chunk_equals_prefill(_m_chunk_offset)

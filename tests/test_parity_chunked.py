@@ -1,0 +1,127 @@
+"""GPU parity of parallax_prefill_chunked (causal prefill against an existing
+cache, also multi-token decode) against the fp64 oracle, through the C ABI.
+
+Error measure as for prefill: per output row, max |gpu - oracle| / max |oracle|,
+bar 2e-3; rows at or past a chunk's length must be exactly zero.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import local_linear_attention_amd as pa
+import oracle
+from workloads import CHUNK_WORKLOAD, WORKLOADS, make_chunk_inputs, make_prefill_inputs, replace_shape
+
+TOL = 2e-3
+pytestmark = pytest.mark.gpu
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    zero = den == 0
+    assert np.all(num[zero] == 0), "rows with no keys must be exactly zero"
+    if np.all(zero):
+        return 0.0
+    return float((num[~zero] / den[~zero]).max())
+
+
+def to_dev(inp):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def run(dev):
+    out = pa.prefill_chunked(dev["q"], dev["rho"], dev["k_cache"], dev["v_cache"],
+                             dev["past_lens"], dev["chunk_lens"], dev["scale"])
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(w, **kw):
+    print(f"[chunked parity] B={w.B} T={w.T} past={w.past} Hq={w.H_q} Hkv={w.H_kv} d={w.d} {kw}",
+          flush=True)
+    cpu = make_chunk_inputs(w, **kw)
+    ref = oracle.oracle_chunk_full(cpu["q"], cpu["rho"], cpu["k_cache"], cpu["v_cache"],
+                                   cpu["past_lens"], cpu["chunk_lens"], cpu["scale"])
+    got = run(to_dev(cpu))
+    assert np.isfinite(got).all()
+    err = max(rel_err(got[b, h], r) for (b, h), r in ref.items())
+    print(f"   max rel err {err:.3e}", flush=True)
+    assert err < TOL
+
+
+SMALL = replace_shape(CHUNK_WORKLOAD, B=2, T=160, past=300, H_q=4, H_kv=2)
+
+
+def test_small_chunk():
+    check(SMALL)
+
+
+@pytest.mark.parametrize("past", [0, 1, 31, 32, 33, 127, 500])
+def test_past_offsets(past):
+    check(replace_shape(SMALL, past=past, T=97))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
+def test_multi_token_decode(T):
+    """A few new tokens against a long cache (speculative / multi-token decode)."""
+    check(replace_shape(SMALL, T=T, past=2000))
+
+
+def test_ragged_past_and_chunk_lengths():
+    w = replace_shape(SMALL, B=3)
+    check(w, past_lens=[300, 0, 41], chunk_lens=[160, 77, 0], S_max=500)
+
+
+def test_group_sizes_and_head_dim_64():
+    check(replace_shape(SMALL, H_q=8, H_kv=2))
+    check(replace_shape(SMALL, d=64, q_std=64 ** -0.25, k_std=64 ** -0.25))
+
+
+def test_no_past_equals_prefill():
+    """With every past length 0 the chunked call is the plain causal prefill."""
+    w = replace_shape(WORKLOADS[5], B=2, T=200, H_q=4, H_kv=2)
+    dev = to_dev(make_prefill_inputs(w, seq_lens=[200, 130]))
+    a = pa.prefill(dev["q"], dev["rho"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"])
+    zero = torch.zeros(2, dtype=torch.int32, device="cuda")
+    b = pa.prefill_chunked(dev["q"], dev["rho"], dev["k"], dev["v"], zero, dev["seq_lens"],
+                           dev["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_chunks_reproduce_full_prefill():
+    """Prefilling a sequence in three chunks gives the full prefill's rows."""
+    w = replace_shape(WORKLOADS[5], B=1, T=384, H_q=4, H_kv=2)
+    dev = to_dev(make_prefill_inputs(w))
+    full = pa.prefill(dev["q"], dev["rho"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"])
+    for p0, p1 in [(0, 100), (100, 257), (257, 384)]:
+        T = p1 - p0
+        out = pa.prefill_chunked(dev["q"][:, :, p0:p1].contiguous(),
+                                 dev["rho"][:, :, p0:p1].contiguous(), dev["k"], dev["v"],
+                                 torch.tensor([p0], dtype=torch.int32, device="cuda"),
+                                 torch.tensor([T], dtype=torch.int32, device="cuda"), dev["scale"])
+        torch.cuda.synchronize()
+        a = out.cpu().numpy()[0]
+        b = full.cpu().numpy()[0, :, p0:p1]
+        assert np.abs(a - b).max() <= 1e-4 * np.abs(b).max()
+
+
+@pytest.mark.slow
+def test_chunk_workload_full_size_sampled():
+    w = CHUNK_WORKLOAD
+    print("[chunked parity] full-size chunked-prefill", flush=True)
+    dev = make_chunk_inputs(w, device="cuda")
+    got = run(dev)
+    assert np.isfinite(got).all()
+    cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dev.items()}
+    rng = np.random.default_rng(6)
+    rows = [(b, h, t) for b in range(w.B) for h in range(w.H_q)
+            for t in {0, 1, 511, w.T - 1} | set(rng.integers(0, w.T, 2).tolist())]
+    ex = oracle.oracle_chunk_rows(cpu["q"], cpu["rho"], cpu["k_cache"], cpu["v_cache"],
+                                  cpu["past_lens"], cpu["chunk_lens"], cpu["scale"], rows)
+    err = max(rel_err(got[b, h, t][None], o[None]) for (b, h, t), o in ex.items())
+    print(f"   {len(rows)} sampled rows: {err:.3e}", flush=True)
+    assert err < TOL

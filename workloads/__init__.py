@@ -37,9 +37,12 @@ import torch
 __all__ = [
     "DecodeWorkload",
     "PrefillWorkload",
+    "ChunkWorkload",
     "WORKLOADS",
+    "CHUNK_WORKLOAD",
     "make_decode_inputs",
     "make_prefill_inputs",
+    "make_chunk_inputs",
     "replace_shape",
 ]
 
@@ -84,6 +87,25 @@ class PrefillWorkload:
     seed: int = 0
 
 
+@dataclasses.dataclass(frozen=True)
+class ChunkWorkload:
+    """Causal prefill of a chunk of T rows after `past` cached tokens."""
+    name: str
+    B: int
+    T: int
+    past: int
+    H_q: int
+    H_kv: int
+    d: int
+    dtype: torch.dtype
+    q_std: float
+    k_std: float
+    v_std: float
+    rho_std: float
+    scale: float
+    seed: int = 0
+
+
 _D128 = 128 ** -0.25
 
 WORKLOADS = {
@@ -98,6 +120,12 @@ WORKLOADS = {
     5: PrefillWorkload("causal-prefill", 4, 4096, 16, 8, 128, torch.bfloat16,
                        _D128, _D128, 1.0, 0.05, 1.0, seed=1005),
 }
+
+
+# Chunked prefill (prefill against an existing cache): the last quarter of the
+# causal-prefill workload, 1024 new rows after 3072 cached tokens.
+CHUNK_WORKLOAD = ChunkWorkload("chunked-prefill", 4, 1024, 3072, 16, 8, 128, torch.bfloat16,
+                               _D128, _D128, 1.0, 0.05, 1.0, seed=1006)
 
 
 def replace_shape(w, **kw):
@@ -186,3 +214,33 @@ def make_prefill_inputs(w: PrefillWorkload, seed=None, device="cpu", seq_lens=No
                 k[b, :, n:] = float("nan")
                 v[b, :, n:] = float("nan")
     return dict(q=q, rho=rho, k=k, v=v, seq_lens=lens, scale=float(w.scale))
+
+
+def make_chunk_inputs(w: ChunkWorkload, seed=None, device="cpu", past_lens=None,
+                      chunk_lens=None, S_max=None, nan_pad=True):
+    """Seeded chunked-prefill inputs for workload ``w``.
+
+    Returns q, rho [B, H_q, T, d] (the chunk's rows); k_cache, v_cache
+    [B, H_kv, S_max, d] (S_max >= past + T, default exactly that) holding the
+    past and the chunk's own keys and values; past_lens, chunk_lens int32 [B]
+    (defaults: w.past and w.T for every sequence); ``scale``. Cache rows at or
+    past past_lens[b] + chunk_lens[b] are NaN.
+    """
+    seed = w.seed if seed is None else seed
+    g = _gen(device, seed)
+    B, T, Hq, Hkv, d = w.B, w.T, w.H_q, w.H_kv, w.d
+    past = torch.as_tensor([w.past] * B if past_lens is None else past_lens).to(torch.int32)
+    lens = torch.as_tensor([T] * B if chunk_lens is None else chunk_lens).to(torch.int32)
+    S = int(S_max) if S_max is not None else int(past.max()) + T
+    q = _normal((B, Hq, T, d), w.q_std, w.dtype, g, device)
+    k = _normal((B, Hkv, S, d), w.k_std, w.dtype, g, device)
+    v = _normal((B, Hkv, S, d), w.v_std, w.dtype, g, device)
+    rho = _normal((B, Hq, T, d), w.rho_std, w.dtype, g, device)
+    if nan_pad:
+        for b in range(B):
+            end = int(past[b]) + int(lens[b])
+            if end < S:
+                k[b, :, end:] = float("nan")
+                v[b, :, end:] = float("nan")
+    return dict(q=q, rho=rho, k_cache=k, v_cache=v, past_lens=past.to(device),
+                chunk_lens=lens.to(device), scale=float(w.scale))
