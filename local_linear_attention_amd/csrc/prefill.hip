@@ -34,7 +34,8 @@
 // 8 key-slot rows, d/16 contiguous dims each, and hands dim j of every row to
 // N-tile j (output column c of tile j is dim (d/16) c + j). Softmax rescaling
 // is lazy (only when a block's max exceeds the running reference by more than
-// 2^8). Heavy (late) row blocks are dispatched first.
+// 2^8). Each workgroup handles a heavy (late) and a light (early) row block,
+// so every workgroup carries the same causal work.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -60,17 +61,14 @@ struct Pre {
   static constexpr int TILE = kKeys * LSTR;           // bytes of one staged tile
 };
 
+// One row block (128 query rows starting at rb * 128) of one (b, h).
 template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+__device__ __forceinline__ void prefill_rows(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ past_lens, float* __restrict__ out, int H_q, int H_kv, int G, int T,
-    int S_max, float scale_log2) {
+    int S_max, float scale_log2, int rb, char (&kv_lds)[2][2][Pre<D>::TILE]) {
   using P = Pre<D>;
-  __shared__ __attribute__((aligned(16))) char kv_lds[2][2][P::TILE];  // [buffer][K, V]
-
-  const int nrb = (T + kRows - 1) / kRows;
-  const int rb = nrb - 1 - (int)blockIdx.x;  // late (heavy) row blocks first
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int hk = h / G;
@@ -339,11 +337,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 }
 
+// Workgroup x handles row blocks nrb - 1 - x and x of one (b, h): under the
+// causal mask their key counts add up to the same total for every x, so all
+// workgroups carry equal work and the short early row blocks never form a
+// tail of their own.
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
+    const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ past_lens, float* __restrict__ out, int H_q, int H_kv, int G, int T,
+    int S_max, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) char kv_lds[2][2][Pre<D>::TILE];  // [buffer][K, V]
+  const int nrb = (T + kRows - 1) / kRows;
+  const int x = blockIdx.x;
+  prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, H_q, H_kv, G, T, S_max, scale_log2,
+                  nrb - 1 - x, kv_lds);
+  if (x != nrb - 1 - x) {
+    __syncthreads();
+    prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, H_q, H_kv, G, T, S_max, scale_log2,
+                    x, kv_lds);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int nrb = (a.T + kRows - 1) / kRows;
-  dim3 grid(nrb, a.H_q, a.B);
+  dim3 grid((nrb + 1) / 2, a.H_q, a.B);  // row blocks paired heavy + light
   if (a.d == 64) {
     hipLaunchKernelGGL((prefill_kernel<64>), grid, dim3(kThreads), 0, st,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
