@@ -79,7 +79,7 @@ __device__ __forceinline__ void prefill_rows(
   const int R0 = rb * kRows;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int g = lane >> 4;     // lane group
   const int c = lane & 15;     // query row within the wave (score layout) / output column
@@ -104,16 +104,25 @@ __device__ __forceinline__ void prefill_rows(
     const bool live = my_row < n;
     const __bf16* qp = q + qbase + (size_t)(live ? my_row : 0) * D + 8 * g;
     const __bf16* rp = rho + qbase + (size_t)(live ? my_row : 0) * D + 8 * g;
+    // With a negative scale, q is negated (exact in bf16) so that the scale
+    // applied below is non-negative and the max of the raw scores gives the
+    // max of the scaled ones.
+    const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < P::KST; ++kk) {
       uint4 a = *reinterpret_cast<const uint4*>(qp + 32 * kk);
       uint4 r = *reinterpret_cast<const uint4*>(rp + 32 * kk);
       if (!live) a = r = uint4{0u, 0u, 0u, 0u};
+      a.x ^= qsign;
+      a.y ^= qsign;
+      a.z ^= qsign;
+      a.w ^= qsign;
       qop[kk] = as_bf16x8(a.x, a.y, a.z, a.w);
       rop[kk] = as_bf16x8(r.x, r.y, r.z, r.w);
     }
   }
 
+  const float sl = fabsf(scale_log2);  // scale in log2 units, applied to the raw scores
   const size_t kvslice = ((size_t)b * H_kv + hk) * (size_t)S_max * D;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + kvslice, (uint32_t)(past + n) * P::ROWB);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + kvslice, (uint32_t)(past + n) * P::ROWB);
@@ -169,16 +178,18 @@ __device__ __forceinline__ void prefill_rows(
   float m = -INFINITY;  // running max (log2 units) of row my_row
   float lsum = 0.f;     // this lane's part of l (its 8 keys per block)
   float bsum = 0.f;     // this lane's part of Bs
-  float cref = 0.f;     // rho_t . k_0
+  f32x4 rinit = {0.f, 0.f, 0.f, 0.f};  // start of the rho . k accumulators: -rho_t . k_0
 
   // Contracts key block kb (LDS buffer buf) into this wave's accumulators.
   auto contract = [&](int kb, int buf) {
-    // ---- transposed scores: lane (g, c) holds row my_row, keys 16 T + 4 g + i
+    // ---- transposed scores: lane (g, c) holds row my_row, keys 16 T + 4 g + i.
+    // The rho . k accumulators start at -c (c = rho_t . k_0, known from block
+    // 0 on), so they come out already relative to the reference.
     f32x4 sc[2], rc[2];
 #pragma unroll
     for (int T2 = 0; T2 < 2; ++T2) {
       sc[T2] = f32x4{0.f, 0.f, 0.f, 0.f};
-      rc[T2] = sc[T2];
+      rc[T2] = rinit;
       const char* krow = &kv_lds[buf][0][(16 * T2 + c) * P::LSTR + 16 * g];
 #pragma unroll
       for (int kk = 0; kk < P::KST; ++kk) {
@@ -187,26 +198,29 @@ __device__ __forceinline__ void prefill_rows(
         rc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rop[kk], rc[T2], 0, 0, 0);
       }
     }
-    if (kb == 0) cref = __shfl(rc[0][0], c);  // key 0 sits in lane (0, c), slot 0
+    if (kb == 0) {
+      const float cref = __shfl(rc[0][0], c);  // key 0 sits in lane (0, c), slot 0
+      rinit = f32x4{-cref, -cref, -cref, -cref};
+#pragma unroll
+      for (int T2 = 0; T2 < 2; ++T2) rc[T2] -= cref;
+    }
 
-    // Scaled scores (log2 units); masked keys are -inf on the block that
-    // reaches past this wave's first row.
-    float x[8];
+    // Raw scores; masked keys are -inf on the block that reaches past this
+    // wave's first row. The weights are exp2(sl s - m), with the scaled max
+    // sl max(s) (sl >= 0).
     float mx = -INFINITY;
-    if (kb * kKeys + kKeys - 1 > past + wrow0) {
+    const bool diag = kb * kKeys + kKeys - 1 > past + wrow0;
+    if (diag) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = kb * kKeys + 16 * (e >> 2) + 4 * g + (e & 3);
-        x[e] = key <= my_pos ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[e]);
+        mx = fmaxf(mx, key <= my_pos ? sc[e >> 2][e & 3] : -INFINITY);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = sc[e >> 2][e & 3] * scale_log2;
-        mx = fmaxf(mx, x[e]);
-      }
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[e >> 2][e & 3]);
     }
+    mx *= sl;
 
     // Lazy rescale. The reference m of a row only has to bound every weight
     // exp2(x - m) by 2^8, so each lane checks its own 8 keys; the row max
@@ -235,13 +249,23 @@ __device__ __forceinline__ void prefill_rows(
 
     // ---- weights e and e (r - c) as packed bf16 high parts and the bf16
     // rounding of the remainders: the A operands of the value MFMAs
+    float ev[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ev[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 2][e & 3], sl, -m));
+    if (diag) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kb * kKeys + 16 * (e >> 2) + 4 * g + (e & 3);
+        ev[e] = key <= my_pos ? ev[e] : 0.f;
+      }
+    }
     uint32_t phw[4], plw[4], qhw[4], qlw[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float e0 = __builtin_amdgcn_exp2f(x[2 * u] - m);
-      const float e1 = __builtin_amdgcn_exp2f(x[2 * u + 1] - m);
-      const float f0 = e0 * (rc[u >> 1][(2 * u) & 3] - cref);
-      const float f1 = e1 * (rc[u >> 1][(2 * u + 1) & 3] - cref);
+      const float e0 = ev[2 * u];
+      const float e1 = ev[2 * u + 1];
+      const float f0 = e0 * rc[u >> 1][(2 * u) & 3];
+      const float f1 = e1 * rc[u >> 1][(2 * u + 1) & 3];
       lsum += e0 + e1;
       bsum += f0 + f1;
       const uint32_t ph = pack_bf16(e0, e1);
@@ -323,9 +347,10 @@ __device__ __forceinline__ void prefill_rows(
     if (t >= T) continue;
     float ov[P::DPL];
     if (t < n) {
-      const float gain = 1.f + bsr / l;
+      const float inv_l = 1.f / l;
+      const float gain = 1.f + bsr * inv_l;
 #pragma unroll
-      for (int j = 0; j < P::DPL; ++j) ov[j] = (accA[j][i] * gain - accC[j][i]) / l;
+      for (int j = 0; j < P::DPL; ++j) ov[j] = (accA[j][i] * gain - accC[j][i]) * inv_l;
     } else {
 #pragma unroll
       for (int j = 0; j < P::DPL; ++j) ov[j] = 0.f;
