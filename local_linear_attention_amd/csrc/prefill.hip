@@ -20,9 +20,8 @@
 // Tiling. A workgroup of 8 waves owns 128 query rows of one (b, h); each wave
 // owns 16 rows, so a wave needs about 210 registers and two waves share each
 // SIMD (one wave's softmax arithmetic overlaps the other's matrix work). Key
-// blocks of 32 keys are staged in double-buffered LDS (rows padded by 16
-// bytes against bank conflicts), shared by the 8 waves, and loaded two blocks
-// before use. Per wave and key block, v_mfma_f32_16x16x32_bf16 computes the
+// blocks of 32 keys are staged in double-buffered LDS (rows padded against
+// bank conflicts), shared by the 8 waves, and loaded two blocks before use. Per wave and key block, v_mfma_f32_16x16x32_bf16 computes the
 // transposed scores S^T = K Q^T and R^T = K rho^T for two 16-key tiles: lane
 // (g = lane / 16, c = lane % 16) holds query row c for keys 16 T + 4 g + i
 // (T = 0, 1; i = 0..3), which are exactly the 8 key slots that lane supplies
@@ -30,9 +29,10 @@
 // statistics need two exchanges (lanes ^ 16, ^ 32). The value MFMA computes
 // [e; e r] V with e and e r each split into a bf16 high part and the bf16
 // rounding of the remainder (four products), so the fp32 weights reach the
-// bf16 contraction to about 2^-17. V needs no transpose: each lane reads its
-// 8 key-slot rows, d/16 contiguous dims each, and hands dim j of every row to
-// N-tile j (output column c of tile j is dim (d/16) c + j). Softmax rescaling
+// bf16 contraction to about 2^-17. The V operand (key slots down, dims
+// across) comes straight from the row-major V tile through the CDNA4
+// transposing LDS load (ds_read_b64_tr_b16), so no lane shuffles V in
+// registers; output column c of N-tile j is dim 16 j + c. Softmax rescaling
 // is lazy (only when a block's max exceeds the running reference by more than
 // 2^8). Each workgroup handles a heavy (late) and a light (early) row block,
 // so every workgroup carries the same causal work.
@@ -53,12 +53,16 @@ constexpr float kRescaleLog2 = 8.0f;
 template <int D>
 struct Pre {
   static constexpr int ROWB = D * 2;                  // bytes per bf16 row
-  static constexpr int LSTR = ROWB + 16;              // padded LDS row stride (bytes)
+  // Padded LDS row strides (bytes): K rows are read 16 rows x 16 bytes at a
+  // time (a 16-byte pad spreads them over all banks); V rows are read by the
+  // transposing load 8 rows x 32 bytes at a time (a 32-byte pad does).
+  static constexpr int LSTR = ROWB + 16;
+  static constexpr int VSTR = ROWB + 32;
   static constexpr int KST = D / 32;                  // k-steps of the score MFMA
-  static constexpr int DPL = D / 16;                  // value dims per lane column = N-tiles
+  static constexpr int DPL = D / 16;                  // N-tiles of the value MFMA
   static constexpr int PIECES = kKeys * ROWB / 16;    // 16-byte pieces per K (or V) tile
   static constexpr int PPT = 2 * PIECES / kThreads;   // pieces per thread per block (K and V)
-  static constexpr int TILE = kKeys * LSTR;           // bytes of one staged tile
+  static constexpr int TILE = kKeys * VSTR;           // bytes of one staged K or V tile
 };
 
 // One row block (128 query rows starting at rb * 128) of one (b, h).
@@ -165,7 +169,7 @@ __device__ __forceinline__ void prefill_rows(
       piece(i, which, idx);
       const int r = idx / (P::ROWB / 16);
       const int c16 = idx % (P::ROWB / 16);
-      *reinterpret_cast<i32x4*>(&kv_lds[buf][which][r * P::LSTR + c16 * 16]) = src[i];
+      *reinterpret_cast<i32x4*>(&kv_lds[buf][which][r * (which ? P::VSTR : P::LSTR) + c16 * 16]) = src[i];
     }
   };
 
@@ -280,28 +284,23 @@ __device__ __forceinline__ void prefill_rows(
     const bf16x8 a_qh = as_bf16x8(qhw[0], qhw[1], qhw[2], qhw[3]);
     const bf16x8 a_ql = as_bf16x8(qlw[0], qlw[1], qlw[2], qlw[3]);
 
-    // ---- V rows of this lane's key slots e: key 16 (e / 4) + 4 g + e % 4,
-    // dims (d/16) c .. (d/16) c + d/16 - 1
-    uint32_t vw[8][P::DPL / 2];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const char* vp = &kv_lds[buf][1][(16 * (e >> 2) + 4 * g + (e & 3)) * P::LSTR + c * (2 * P::DPL)];
-      if constexpr (P::DPL == 8) {
-        const i32x4 w = *reinterpret_cast<const i32x4*>(vp);
-#pragma unroll
-        for (int z = 0; z < 4; ++z) vw[e][z] = (uint32_t)w[z];
-      } else {
-        const i32x2 w = *reinterpret_cast<const i32x2*>(vp);
-        vw[e][0] = (uint32_t)w[0];
-        vw[e][1] = (uint32_t)w[1];
-      }
-    }
+    // ---- value MFMAs. The B operand of N-tile j (dims 16 j .. 16 j + 15) in
+    // lane (g, c) is V at dim 16 j + c for key slots e = 0..7 (keys
+    // 16 (e / 4) + 4 g + e % 4). Each half (e < 4, e >= 4) comes from one
+    // transposing LDS load: within a group of 16 lanes, lane 4 a + b receives
+    // element b of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and
+    // a + 12, so lane s of group g addresses key 16 h + 4 g + s / 4 at dims
+    // 16 j + 4 (s % 4) .. + 3.
+    const char* vbase = &kv_lds[buf][1][(4 * g + (c >> 2)) * P::VSTR + 8 * (c & 3)];
 #pragma unroll
     for (int j = 0; j < P::DPL; ++j) {
-      uint32_t bw[4];
-#pragma unroll
-      for (int z = 0; z < 4; ++z) bw[z] = pair_halves(vw[2 * z][j >> 1], vw[2 * z + 1][j >> 1], j & 1);
-      const bf16x8 vop = as_bf16x8(bw[0], bw[1], bw[2], bw[3]);
+      typedef short i16x4 __attribute__((ext_vector_type(4)));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * j));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * j + 16 * P::VSTR));
+      const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
       accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ph, vop, accA[j], 0, 0, 0);
       accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pl, vop, accA[j], 0, 0, 0);
       accC[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_qh, vop, accC[j], 0, 0, 0);
@@ -355,10 +354,9 @@ __device__ __forceinline__ void prefill_rows(
 #pragma unroll
       for (int j = 0; j < P::DPL; ++j) ov[j] = 0.f;
     }
-    float* dst = obase + (size_t)t * D + P::DPL * c;
+    float* dst = obase + (size_t)t * D + c;  // column c of N-tile j is dim 16 j + c
 #pragma unroll
-    for (int j = 0; j < P::DPL; j += 4)
-      *reinterpret_cast<float4*>(dst + j) = float4{ov[j], ov[j + 1], ov[j + 2], ov[j + 3]};
+    for (int j = 0; j < P::DPL; ++j) dst[16 * j] = ov[j];
   }
 }
 
