@@ -268,7 +268,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads", choices=["all", "main", "prefill"], default="all",
                     help="all: every workload; main: the GQA decode line only; "
-                         "prefill: the causal prefill only (for profiling)")
+                         "prefill: the causal and chunked prefill only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -298,8 +298,10 @@ def main():
 
     if args.workloads == "prefill":
         log("workload causal-prefill")
-        res = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 3)
-        print(json.dumps({"workload": WORKLOADS[5].name, **res}), flush=True)
+        res = {WORKLOADS[5].name: bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10)}
+        log("workload chunked-prefill")
+        res[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
+        print(json.dumps({"workloads": res}), flush=True)
         return
 
     w = WORKLOADS[2]
@@ -358,9 +360,9 @@ def main():
             del r
             torch.cuda.empty_cache()
         log("workload causal-prefill")
-        workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 3)
+        workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10)
         log("workload chunked-prefill")
-        workloads[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 3)
+        workloads[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
     result["workloads"] = workloads
 
     if not args.no_cpu_baseline:
