@@ -28,6 +28,11 @@ Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 something other than itself (a library routine, brute force, a closed form,
 an exact worked example, invariants, and the textbook local-linear
 regression it reduces to). No function is "parity unpinned".
+
+``lla_oracle`` adds the solver-based Local Linear Attention that Parallax
+replaces (conjugate gradient for the probe), pinned in
+``tests/test_lla_oracle_pins.py``; ``lla_contrast`` measures its accuracy and
+cost against softmax attention on synthetic data.
 """
 
 from .parallax_oracle import (  # noqa: F401
