@@ -32,7 +32,9 @@ regression it reduces to). No function is "parity unpinned".
 ``lla_oracle`` adds the solver-based Local Linear Attention that Parallax
 replaces (conjugate gradient for the probe), pinned in
 ``tests/test_lla_oracle_pins.py``; ``lla_contrast`` measures its accuracy and
-cost against softmax attention on synthetic data.
+cost against softmax attention on synthetic data. ``parallax_grad_oracle``
+gives the gradients of the causal prefill (fp64 autograd of the explicit
+definition), pinned in ``tests/test_grad_oracle_pins.py``.
 """
 
 from .parallax_oracle import (  # noqa: F401
@@ -46,3 +48,4 @@ from .parallax_oracle import (  # noqa: F401
     oracle_chunk_rows,
     oracle_chunk_full,
 )
+from .parallax_grad_oracle import oracle_prefill_grads  # noqa: F401
