@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 1
+#define PARALLAX_ABI_VERSION 2
 
 typedef enum {
   PARALLAX_OK = 0,
@@ -189,6 +189,48 @@ parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const
                                            const int32_t* chunk_lens, float* out, int B, int H_q,
                                            int H_kv, int d, int T, int S_max, float scale,
                                            parallax_dtype_t dtype, void* stream);
+
+/* Causal prefill for training: parallax_prefill plus what the backward
+ * needs. Besides `out` it writes
+ *   mu_v   [B, H_q, T, d] fp32: the softmax-attention part sum_j w_j v_j;
+ *   stats  [B, H_q, T, 4] fp32: per row (log2 of sum_j 2^(scale log2(e) q.k_j),
+ *          c = rho . k_0, rbar - c, 0), where rbar = sum_j w_j rho . k_j.
+ * Rows t >= seq_lens[b] get zeros in all three. The gradients are those of
+ * the output of the blog "Parallax: Breaking the Boundary Bias with
+ * Parameterized Local Linear Attention", "The Core Insight: Covariance
+ * Correction", output equation, with the learned probe of the paper page
+ * "Parallax: Parameterized Local Linear Attention for Language Modeling",
+ * "Abstract". Arguments, errors and semantics otherwise as parallax_prefill;
+ * mu_v and stats must be 16-byte aligned device pointers. */
+parallax_status_t parallax_prefill_train(const void* q, const void* rho, const void* k,
+                                         const void* v, const int32_t* seq_lens, float* out,
+                                         float* mu_v, float* stats, int B, int H_q, int H_kv,
+                                         int d, int T, int S_max, float scale,
+                                         parallax_dtype_t dtype, void* stream);
+
+/* Bytes of workspace parallax_prefill_backward needs: dO split into bf16
+ * high and low parts (2 x B H_q T d x 2 bytes) and two floats per row,
+ * rounded to 16 bytes; 0 for non-positive sizes. */
+size_t parallax_prefill_backward_workspace_size(int B, int H_q, int T, int d);
+
+/* Gradients of the causal prefill output for an upstream gradient
+ * dout [B, H_q, T, d] fp32, from the inputs of parallax_prefill_train and its
+ * out, mu_v and stats:
+ *   dq, drho  [B, H_q, T, d] fp32 (rows t >= seq_lens[b] are 0);
+ *   dk, dv    [B, H_kv, S_max, d] fp32, summed over the H_q / H_kv query heads
+ *             of each KV head (keys j >= seq_lens[b] are 0).
+ * Every output is written in full. Rows of dout at or past seq_lens[b] are
+ * ignored. `workspace` (device, 16-byte aligned, caller-owned, at least
+ * parallax_prefill_backward_workspace_size bytes) is overwritten. Three
+ * launches on `stream`, asynchronous; nothing is allocated. Errors as
+ * parallax_prefill, plus PARALLAX_ERR_WORKSPACE for a short workspace; on an
+ * error nothing is launched. Deterministic: no atomics, fixed reduction
+ * order. */
+parallax_status_t parallax_prefill_backward(
+    const void* q, const void* rho, const void* k, const void* v, const int32_t* seq_lens,
+    const float* out, const float* mu_v, const float* stats, const float* dout, float* dq,
+    float* drho, float* dk, float* dv, int B, int H_q, int H_kv, int d, int T, int S_max,
+    float scale, parallax_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

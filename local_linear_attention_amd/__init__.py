@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "ParallaxError", "lib", "library_path", "abi_version", "status_string", "decode_plan",
     "decode_workspace_size", "decode", "decode_partial", "decode_combine", "prefill",
-    "prefill_chunked", "STATUS", "EXPORTED_SYMBOLS",
+    "prefill_chunked", "prefill_train", "prefill_backward_workspace_size", "prefill_backward",
+    "STATUS", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +44,8 @@ EXPORTED_SYMBOLS = (
     "parallax_abi_version", "parallax_status_string", "parallax_decode_plan",
     "parallax_decode_workspace_size", "parallax_decode", "parallax_decode_partial",
     "parallax_decode_combine", "parallax_prefill", "parallax_prefill_chunked",
+    "parallax_prefill_train", "parallax_prefill_backward_workspace_size",
+    "parallax_prefill_backward",
 )
 
 
@@ -94,6 +97,12 @@ def load_library(path: str) -> ctypes.CDLL:
     L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.parallax_prefill_chunked.restype = i
     L.parallax_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.parallax_prefill_train.restype = i
+    L.parallax_prefill_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.parallax_prefill_backward_workspace_size.restype = sz
+    L.parallax_prefill_backward_workspace_size.argtypes = [i, i, i, i]
+    L.parallax_prefill_backward.restype = i
+    L.parallax_prefill_backward.argtypes = [vp] * 13 + [i, i, i, i, i, i, f, i, vp, sz, vp]
     return L
 
 
@@ -263,3 +272,74 @@ def prefill_chunked(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: floa
             past_lens.data_ptr(), chunk_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, T, S_max,
             float(scale), _dtype_code(q), _stream_ptr(q.device)), "parallax_prefill_chunked")
     return out
+
+
+def _prefill_shapes(q, rho, k, v, seq_lens):
+    for name, t in (("q", q), ("rho", rho), ("k", k), ("v", v), ("seq_lens", seq_lens)):
+        _dev_tensor(t, name)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q is [B, H_q, T, d] and k is [B, H_kv, S_max, d]")
+    B, H_q, T, d = q.shape
+    _, H_kv, S_max, _ = k.shape
+    if rho.shape != q.shape or v.shape != k.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("inconsistent prefill shapes")
+    if not (q.dtype == rho.dtype == k.dtype == v.dtype):
+        raise TypeError("q, rho, k and v must share one dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    return B, H_q, H_kv, T, S_max, d
+
+
+def prefill_train(q, rho, k, v, seq_lens, scale: float):
+    """Causal prefill that also returns what the backward needs.
+
+    Returns (out, mu_v, stats): out and mu_v [B, H_q, T, d] fp32, stats
+    [B, H_q, T, 4] fp32 (see parallax_prefill_train).
+    """
+    B, H_q, H_kv, T, S_max, d = _prefill_shapes(q, rho, k, v, seq_lens)
+    out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    mu = torch.empty_like(out)
+    stats = torch.empty((B, H_q, T, 4), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_prefill_train(
+            q.data_ptr(), rho.data_ptr(), k.data_ptr(), v.data_ptr(), seq_lens.data_ptr(),
+            out.data_ptr(), mu.data_ptr(), stats.data_ptr(), B, H_q, H_kv, d, T, S_max,
+            float(scale), _dtype_code(q), _stream_ptr(q.device)), "parallax_prefill_train")
+    return out, mu, stats
+
+
+def prefill_backward_workspace_size(B: int, H_q: int, T: int, d: int) -> int:
+    return int(lib().parallax_prefill_backward_workspace_size(B, H_q, T, d))
+
+
+def prefill_backward(q, rho, k, v, seq_lens, out, mu_v, stats, dout, scale: float, *,
+                     workspace=None):
+    """Gradients (dq, drho, dk, dv) of the causal prefill for upstream dout.
+
+    dq, drho are shaped like q; dk, dv like k (summed over each KV head's
+    query heads). See parallax_prefill_backward.
+    """
+    B, H_q, H_kv, T, S_max, d = _prefill_shapes(q, rho, k, v, seq_lens)
+    for name, t in (("out", out), ("mu_v", mu_v), ("stats", stats), ("dout", dout)):
+        _dev_tensor(t, name)
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be fp32")
+    if out.shape != q.shape or mu_v.shape != q.shape or dout.shape != q.shape or \
+            stats.shape != (B, H_q, T, 4):
+        raise ValueError("out, mu_v, dout are [B, H_q, T, d] and stats [B, H_q, T, 4]")
+    need = prefill_backward_workspace_size(B, H_q, T, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dq = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    drho = torch.empty_like(dq)
+    dk = torch.empty((B, H_kv, S_max, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_prefill_backward(
+            q.data_ptr(), rho.data_ptr(), k.data_ptr(), v.data_ptr(), seq_lens.data_ptr(),
+            out.data_ptr(), mu_v.data_ptr(), stats.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+            drho.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H_q, H_kv, d, T, S_max,
+            float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes,
+            _stream_ptr(q.device)), "parallax_prefill_backward")
+    return dq, drho, dk, dv

@@ -262,8 +262,8 @@ parallax_status_t prefill_common(const void* q, const void* rho, const void* k, 
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
       (reinterpret_cast<uintptr_t>(past_lens) & 3u))
     return PARALLAX_ERR_MISALIGNED;
-  parallax::PrefillArgs a{q,     rho,  k,    v,     seq_lens,  past_lens, out, B,
-                          H_q,   H_kv, H_q / H_kv, d, T, S_max,     scale};
+  parallax::PrefillArgs a{q,   rho,  k,          v, seq_lens, past_lens, out, nullptr, nullptr, B,
+                          H_q, H_kv, H_q / H_kv, d, T,        S_max,     scale};
   return hip_status(parallax::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -292,6 +292,112 @@ parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const
     if (!past_lens) return PARALLAX_ERR_NULL_POINTER;
     return prefill_common(q, rho, k_cache, v_cache, chunk_lens, past_lens, out, B, H_q, H_kv, d,
                           T, S_max, scale, dtype, stream);
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+size_t bwd_workspace_bytes(int B, int H_q, int T, int d) {
+  if (B <= 0 || H_q <= 0 || T <= 0 || d <= 0) return 0;
+  const size_t rows = (size_t)B * H_q * T;
+  const size_t half = rows * d * 2;          // one bf16 copy of dO
+  return ((2 * half + rows * 8) + 15) / 16 * 16;
+}
+
+// Shape and pointer checks shared by the training forward and the backward.
+parallax_status_t check_prefill_shape(int B, int H_q, int H_kv, int d, int T, int S_max,
+                                      float scale, parallax_dtype_t dtype) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || T <= 0 || S_max <= 0 || T > S_max ||
+      H_q % H_kv != 0)
+    return PARALLAX_ERR_BAD_SHAPE;
+  if (dtype != PARALLAX_BF16) return PARALLAX_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
+  if (((long long)S_max + 256) * d * 4 >= (1LL << 31) || ((long long)T + 256) * d * 4 >= (1LL << 31))
+    return PARALLAX_ERR_UNSUPPORTED;
+  if (B > 65535 || H_q > 65535) return PARALLAX_ERR_UNSUPPORTED;
+  if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;
+  return PARALLAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+parallax_status_t parallax_prefill_train(const void* q, const void* rho, const void* k,
+                                         const void* v, const int32_t* seq_lens, float* out,
+                                         float* mu_v, float* stats, int B, int H_q, int H_kv,
+                                         int d, int T, int S_max, float scale,
+                                         parallax_dtype_t dtype, void* stream) {
+  try {
+    if (!q || !rho || !k || !v || !seq_lens || !out || !mu_v || !stats)
+      return PARALLAX_ERR_NULL_POINTER;
+    const parallax_status_t st = check_prefill_shape(B, H_q, H_kv, d, T, S_max, scale, dtype);
+    if (st != PARALLAX_OK) return st;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(mu_v) || !aligned16(stats) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+      return PARALLAX_ERR_MISALIGNED;
+    parallax::PrefillArgs a{q,   rho,  k,          v, seq_lens, nullptr, out, mu_v, stats, B,
+                            H_q, H_kv, H_q / H_kv, d, T,        S_max,   scale};
+    return hip_status(parallax::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+size_t parallax_prefill_backward_workspace_size(int B, int H_q, int T, int d) {
+  return bwd_workspace_bytes(B, H_q, T, d);
+}
+
+parallax_status_t parallax_prefill_backward(
+    const void* q, const void* rho, const void* k, const void* v, const int32_t* seq_lens,
+    const float* out, const float* mu_v, const float* stats, const float* dout, float* dq,
+    float* drho, float* dk, float* dv, int B, int H_q, int H_kv, int d, int T, int S_max,
+    float scale, parallax_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!q || !rho || !k || !v || !seq_lens || !out || !mu_v || !stats || !dout || !dq || !drho ||
+        !dk || !dv || !workspace)
+      return PARALLAX_ERR_NULL_POINTER;
+    const parallax_status_t st = check_prefill_shape(B, H_q, H_kv, d, T, S_max, scale, dtype);
+    if (st != PARALLAX_OK) return st;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(mu_v) || !aligned16(stats) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(drho) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+      return PARALLAX_ERR_MISALIGNED;
+    if (workspace_bytes < bwd_workspace_bytes(B, H_q, T, d)) return PARALLAX_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * H_q * T;
+    char* ws = static_cast<char*>(workspace);
+    parallax::BwdArgs a;
+    a.q = q;
+    a.rho = rho;
+    a.k = k;
+    a.v = v;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.mu = mu_v;
+    a.stats = reinterpret_cast<const float4*>(stats);
+    a.dout = dout;
+    a.dq = dq;
+    a.drho = drho;
+    a.dk = dk;
+    a.dv = dv;
+    a.dhi = reinterpret_cast<__bf16*>(ws);
+    a.dlo = reinterpret_cast<__bf16*>(ws + rows * d * 2);
+    a.gd = reinterpret_cast<float2*>(ws + 2 * rows * d * 2);
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = H_q / H_kv;
+    a.d = d;
+    a.T = T;
+    a.S_max = S_max;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return hip_status(parallax::launch_prefill_backward(a, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return PARALLAX_ERR_HIP;
   }

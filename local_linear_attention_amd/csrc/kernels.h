@@ -29,12 +29,38 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   const int32_t* past_lens;  // null: no past (plain causal prefill)
   float* out;
+  float* mu_out;  // training mode: mu_v [B, H_q, T, d] fp32, else null
+  void* stats;    // training mode: [B, H_q, T] x (lse2, c, rbar - c, 0) fp32, else null
   int B, H_q, H_kv, G, d, T, S_max;
   float scale;
+};
+
+// Causal prefill backward. The workspace holds dO split into bf16 high and
+// low parts ([B, H_q, T, d] each) and per-row (G, Dt) = (dO.mu_v, dO.out).
+struct BwdArgs {
+  const void* q;
+  const void* rho;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const float* out;
+  const float* mu;
+  const float4* stats;
+  const float* dout;
+  float* dq;
+  float* drho;
+  float* dk;
+  float* dv;
+  __bf16* dhi;
+  __bf16* dlo;
+  float2* gd;
+  int B, H_q, H_kv, G, d, T, S_max;
+  float scale, scale_log2;
 };
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st);
 
 }  // namespace parallax

@@ -70,8 +70,9 @@ template <int D>
 __device__ __forceinline__ void prefill_rows(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ past_lens, float* __restrict__ out, int H_q, int H_kv, int G, int T,
-    int S_max, float scale_log2, int rb, char (&kv_lds)[2][2][Pre<D>::TILE]) {
+    const int32_t* __restrict__ past_lens, float* __restrict__ out, float* __restrict__ mu_out,
+    float4* __restrict__ stats, int H_q, int H_kv, int G, int T, int S_max, float scale_log2, int rb,
+    char (&kv_lds)[2][2][Pre<D>::TILE]) {
   using P = Pre<D>;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -96,8 +97,15 @@ __device__ __forceinline__ void prefill_rows(
   if (R0 >= n) {  // whole block past the sequence: zeros
     for (int i = tid; i < kRows * D / 4; i += kThreads) {
       const int r = R0 + i / (D / 4);
-      if (r < T) reinterpret_cast<float4*>(obase + (size_t)r * D)[i % (D / 4)] = float4{0.f, 0.f, 0.f, 0.f};
+      if (r < T) {
+        reinterpret_cast<float4*>(obase + (size_t)r * D)[i % (D / 4)] = float4{0.f, 0.f, 0.f, 0.f};
+        if (mu_out)
+          reinterpret_cast<float4*>(mu_out + qbase + (size_t)r * D)[i % (D / 4)] = float4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+    if (stats)
+      for (int r = R0 + tid; r < min(R0 + kRows, T); r += kThreads)
+        stats[((size_t)b * H_q + h) * T + r] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
 
@@ -342,21 +350,29 @@ __device__ __forceinline__ void prefill_rows(
     const int lr = 4 * g + i;  // row within the wave held by this lane's accumulators
     const float l = __shfl(ltot, lr);
     const float bsr = __shfl(btot, lr);
+    // training mode: the row's m and reference c live in the lanes whose column is lr
+    const float mrow = __shfl(m, lr);
+    const float crow = -__shfl(rinit[0], lr);
     const int t = wrow0 + lr;
     if (t >= T) continue;
     float ov[P::DPL];
-    if (t < n) {
-      const float inv_l = 1.f / l;
-      const float gain = 1.f + bsr * inv_l;
+    const bool live = t < n;
+    const float inv_l = live ? 1.f / l : 0.f;
+    const float gain = 1.f + bsr * inv_l;
 #pragma unroll
-      for (int j = 0; j < P::DPL; ++j) ov[j] = (accA[j][i] * gain - accC[j][i]) * inv_l;
-    } else {
-#pragma unroll
-      for (int j = 0; j < P::DPL; ++j) ov[j] = 0.f;
-    }
+    for (int j = 0; j < P::DPL; ++j) ov[j] = live ? (accA[j][i] * gain - accC[j][i]) * inv_l : 0.f;
     float* dst = obase + (size_t)t * D + c;  // column c of N-tile j is dim 16 j + c
 #pragma unroll
     for (int j = 0; j < P::DPL; ++j) dst[16 * j] = ov[j];
+    if (mu_out) {  // mu_v = A / l
+      float* mdst = mu_out + qbase + (size_t)t * D + c;
+#pragma unroll
+      for (int j = 0; j < P::DPL; ++j) mdst[16 * j] = accA[j][i] * inv_l;
+    }
+    // (log2-sum-exp of the scaled scores, reference c = rho . k_0, Bs / l = rbar - c)
+    if (stats && c == 0)
+      stats[((size_t)b * H_q + h) * T + t] =
+          live ? float4{mrow + __builtin_log2f(l), crow, bsr * inv_l, 0.f} : float4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -368,17 +384,17 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ past_lens, float* __restrict__ out, int H_q, int H_kv, int G, int T,
-    int S_max, float scale_log2) {
+    const int32_t* __restrict__ past_lens, float* __restrict__ out, float* __restrict__ mu_out,
+    float4* __restrict__ stats, int H_q, int H_kv, int G, int T, int S_max, float scale_log2) {
   __shared__ __attribute__((aligned(16))) char kv_lds[2][2][Pre<D>::TILE];  // [buffer][K, V]
   const int nrb = (T + kRows - 1) / kRows;
   const int x = blockIdx.x;
-  prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, H_q, H_kv, G, T, S_max, scale_log2,
-                  nrb - 1 - x, kv_lds);
+  prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
+                  scale_log2, nrb - 1 - x, kv_lds);
   if (x != nrb - 1 - x) {
     __syncthreads();
-    prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, H_q, H_kv, G, T, S_max, scale_log2,
-                    x, kv_lds);
+    prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
+                    scale_log2, x, kv_lds);
   }
 }
 
@@ -391,14 +407,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((prefill_kernel<64>), grid, dim3(kThreads), 0, st,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
                        static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                       a.seq_lens, a.past_lens, a.out, a.H_q, a.H_kv, a.G, a.T, a.S_max,
-                       a.scale * kLog2e);
+                       a.seq_lens, a.past_lens, a.out, a.mu_out, static_cast<float4*>(a.stats), a.H_q,
+                       a.H_kv, a.G, a.T, a.S_max, a.scale * kLog2e);
   } else {
     hipLaunchKernelGGL((prefill_kernel<128>), grid, dim3(kThreads), 0, st,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
                        static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                       a.seq_lens, a.past_lens, a.out, a.H_q, a.H_kv, a.G, a.T, a.S_max,
-                       a.scale * kLog2e);
+                       a.seq_lens, a.past_lens, a.out, a.mu_out, static_cast<float4*>(a.stats), a.H_q,
+                       a.H_kv, a.G, a.T, a.S_max, a.scale * kLog2e);
   }
   return hipGetLastError();
 }

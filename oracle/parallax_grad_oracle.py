@@ -53,11 +53,13 @@ def prefill_head_torch(Q, R, K, V, scale: float):
     return mu_v - (WR @ V - WR.sum(dim=1, keepdim=True) * mu_v)
 
 
-def oracle_prefill_grads(q, rho, k, v, seq_lens, dout, scale: float):
+def oracle_prefill_grads(q, rho, k, v, seq_lens, dout, scale: float, kv_heads=None):
     """Gradients of the causal prefill for upstream gradient `dout`.
 
     q, rho, dout: [B, H_q, T, d]; k, v: [B, H_kv, S_max, d]; seq_lens: [B].
     Returns (dq, drho, dk, dv) as fp64 NumPy arrays shaped like q, rho, k, v.
+    `kv_heads` (list of (b, h_kv)) restricts the work to those KV heads and
+    the query heads of their groups; everything else is left zero.
     """
     q, rho, k, v, dout = (_t64(x) for x in (q, rho, k, v, dout))
     lens = np.asarray(_t64(seq_lens).numpy(), dtype=np.int64)
@@ -74,6 +76,8 @@ def oracle_prefill_grads(q, rho, k, v, seq_lens, dout, scale: float):
             continue
         for h in range(H_q):
             hk = h // G
+            if kv_heads is not None and (b, hk) not in kv_heads:
+                continue
             Q = q[b, h, :n].clone().requires_grad_(True)
             R = rho[b, h, :n].clone().requires_grad_(True)
             K = k[b, hk, :n].clone().requires_grad_(True)

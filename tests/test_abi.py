@@ -38,7 +38,7 @@ def header_functions():
 
 def test_header_symbols_exported(L):
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 12
     assert set(names) == set(pa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -169,3 +169,54 @@ def test_prefill_chunked_argument_errors(L):
     assert call(dtype=F32) == UNSUP
     assert call(past=P + 2) == MISAL
     assert call(q=P + 8) == MISAL
+
+
+def _train(L, q=P, rho=P, k=P, v=P, lens=P, out=P, mu=P, st=P, B=1, Hq=2, Hkv=1, d=128, T=256,
+           S=256, scale=1.0, dtype=BF16):
+    return L.parallax_prefill_train(q, rho, k, v, lens, out, mu, st, B, Hq, Hkv, d, T, S, scale,
+                                    dtype, None)
+
+
+def test_prefill_train_argument_errors(L):
+    assert _train(L, mu=0) == NULLP
+    assert _train(L, st=0) == NULLP
+    assert _train(L, T=0) == SHAPE
+    assert _train(L, T=300, S=256) == SHAPE
+    assert _train(L, dtype=F32) == UNSUP
+    assert _train(L, d=96) == UNSUP
+    assert _train(L, mu=P + 4) == MISAL
+    assert _train(L, st=P + 8) == MISAL
+
+
+def test_backward_workspace_size(L):
+    f = L.parallax_prefill_backward_workspace_size
+    # dO high and low parts (bf16) plus (G, Dt) per row
+    assert f(4, 16, 4096, 128) == 2 * 4 * 16 * 4096 * 128 * 2 + 4 * 16 * 4096 * 8
+    assert f(1, 1, 3, 64) == (2 * 3 * 64 * 2 + 3 * 8 + 15) // 16 * 16
+    assert f(0, 1, 3, 64) == 0 and f(1, 1, 0, 64) == 0
+
+
+def _bwd(L, ptrs=None, B=1, Hq=2, Hkv=1, d=128, T=256, S=256, scale=1.0, dtype=BF16, ws=P,
+         ws_bytes=1 << 30):
+    p = [P] * 13 if ptrs is None else ptrs
+    return L.parallax_prefill_backward(*p, B, Hq, Hkv, d, T, S, scale, dtype, ws, ws_bytes, None)
+
+
+def test_prefill_backward_argument_errors(L):
+    for i in range(13):
+        p = [P] * 13
+        p[i] = 0
+        assert _bwd(L, p) == NULLP, i
+    assert _bwd(L, ws=0) == NULLP
+    assert _bwd(L, Hq=3, Hkv=2) == SHAPE
+    assert _bwd(L, T=257, S=256) == SHAPE
+    assert _bwd(L, scale=float("nan")) == SHAPE
+    assert _bwd(L, dtype=F32) == UNSUP
+    assert _bwd(L, d=256) == UNSUP
+    for i in range(13):
+        p = [P] * 13
+        p[i] = P + 8 if i != 4 else P + 2
+        assert _bwd(L, p) == MISAL, i
+    assert _bwd(L, ws=P + 4) == MISAL
+    need = L.parallax_prefill_backward_workspace_size(1, 2, 256, 128)
+    assert _bwd(L, ws_bytes=need - 1) == WS
