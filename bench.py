@@ -176,6 +176,50 @@ def bench_prefill(w, steps, warmup, seed=None):
             "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
 
 
+def bench_backward(w, steps, warmup, seed=None):
+    """Causal-prefill backward (prep + dq/drho + dk/dv launches) per step, and
+    the training forward that saves mu_v and the row statistics."""
+    import torch
+
+    import local_linear_attention_amd as pa
+    from workloads import make_prefill_inputs
+
+    dev = torch.device("cuda:0")
+    inp = make_prefill_inputs(w, seed=seed, device=dev)
+    g = torch.Generator(device=dev).manual_seed(int(w.seed) + 99)
+    dout = torch.randn((w.B, w.H_q, w.T, w.d), generator=g, device=dev, dtype=torch.float32)
+    args = (inp["q"], inp["rho"], inp["k"], inp["v"], inp["seq_lens"])
+    out, mu, stats = pa.prefill_train(*args, inp["scale"])
+    ws = torch.empty(pa.prefill_backward_workspace_size(w.B, w.H_q, w.T, w.d), dtype=torch.uint8,
+                     device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps / 1e3
+
+    t_fwd = timed(lambda: pa.prefill_train(*args, inp["scale"]))
+    t_bwd = timed(lambda: pa.prefill_backward(*args, out, mu, stats, dout, inp["scale"],
+                                              workspace=ws))
+    pairs = w.T * (w.T + 1) / 2 * w.B * w.H_q
+    # algorithmic backward work: the six gradient products (g = dO V^T, dV,
+    # dQ, drho, and dK from q and from rho) plus recomputing s and r: 8
+    # contractions of 2d flops per causal pair (twice the forward's 4)
+    flops = 16.0 * w.d * pairs
+    return {"train_forward_us": t_fwd * 1e6, "backward_us": t_bwd * 1e6,
+            "algorithmic_tflop": flops / 1e12, "tflops": flops / t_bwd / 1e12,
+            "mfma_util": flops / t_bwd / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
+
+
 def bench_chunked(w, steps, warmup, seed=None):
     """Chunked prefill: w.T new rows after w.past cached tokens per sequence."""
     import torch
@@ -274,7 +318,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads", choices=["all", "main", "prefill"], default="all",
                     help="all: every workload; main: the GQA decode line only; "
-                         "prefill: the causal and chunked prefill only (for profiling)")
+                         "prefill: the causal and chunked prefill and the prefill backward "
+                         "only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -307,6 +352,8 @@ def main():
         res = {WORKLOADS[5].name: bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10)}
         log("workload chunked-prefill")
         res[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
+        log("workload causal-prefill-backward")
+        res["causal-prefill-backward"] = bench_backward(WORKLOADS[5], max(5, args.steps // 40), 5)
         print(json.dumps({"workloads": res}), flush=True)
         return
 
@@ -369,6 +416,8 @@ def main():
         workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10)
         log("workload chunked-prefill")
         workloads[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
+        log("workload causal-prefill-backward")
+        workloads["causal-prefill-backward"] = bench_backward(WORKLOADS[5], max(5, args.steps // 40), 5)
     result["workloads"] = workloads
 
     if not args.no_cpu_baseline:
