@@ -220,6 +220,41 @@ def bench_backward(w, steps, warmup, seed=None):
             "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
 
 
+def bench_projection(w, steps, warmup, d_model=None):
+    """Fused q, k, v, rho projection for the causal-prefill shapes: x
+    [B, T, d_model] by the packed weight [(2 H_q + 2 H_kv) d, d_model]
+    (d_model = H_q d unless given), bf16 in, bf16 out."""
+    import torch
+
+    import local_linear_attention_amd as pa
+
+    dev = torch.device("cuda:0")
+    C = w.H_q * w.d if d_model is None else d_model
+    g = torch.Generator(device=dev).manual_seed(int(w.seed) + 123)
+    x = torch.randn((w.B, w.T, C), generator=g, device=dev).to(torch.bfloat16)
+    N = (2 * w.H_q + 2 * w.H_kv) * w.d
+    wt = (torch.randn((N, C), generator=g, device=dev) * C ** -0.5).to(torch.bfloat16)
+    kc = torch.zeros((w.B, w.H_kv, w.T, w.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    run = lambda: pa.qkvr_projection(x, wt, w.H_q, w.H_kv, w.d, k_cache=kc, v_cache=vc)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    kern = ev0.elapsed_time(ev1) / steps / 1e3
+    flops = 2.0 * w.B * w.T * N * C
+    return {"kernel_us": kern * 1e6, "algorithmic_tflop": flops / 1e12,
+            "tflops": flops / kern / 1e12,
+            "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "shape": dict(tokens=w.B * w.T, d_model=C, out_features=N)}
+
+
 def bench_chunked(w, steps, warmup, seed=None):
     """Chunked prefill: w.T new rows after w.past cached tokens per sequence."""
     import torch
@@ -318,8 +353,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads", choices=["all", "main", "prefill"], default="all",
                     help="all: every workload; main: the GQA decode line only; "
-                         "prefill: the causal and chunked prefill and the prefill backward "
-                         "only (for profiling)")
+                         "prefill: the causal and chunked prefill, the prefill backward and "
+                         "the q/k/v/rho projection only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -354,6 +389,8 @@ def main():
         res[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
         log("workload causal-prefill-backward")
         res["causal-prefill-backward"] = bench_backward(WORKLOADS[5], max(5, args.steps // 40), 5)
+        log("workload qkvr-projection")
+        res["qkvr-projection"] = bench_projection(WORKLOADS[5], max(5, args.steps // 10), 10)
         print(json.dumps({"workloads": res}), flush=True)
         return
 
@@ -418,6 +455,8 @@ def main():
         workloads[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
         log("workload causal-prefill-backward")
         workloads["causal-prefill-backward"] = bench_backward(WORKLOADS[5], max(5, args.steps // 40), 5)
+        log("workload qkvr-projection")
+        workloads["qkvr-projection"] = bench_projection(WORKLOADS[5], max(5, args.steps // 10), 10)
     result["workloads"] = workloads
 
     if not args.no_cpu_baseline:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 2
+#define PARALLAX_ABI_VERSION 3
 
 typedef enum {
   PARALLAX_OK = 0,
@@ -231,6 +231,32 @@ parallax_status_t parallax_prefill_backward(
     const float* out, const float* mu_v, const float* stats, const float* dout, float* dq,
     float* drho, float* dk, float* dv, int B, int H_q, int H_kv, int d, int T, int S_max,
     float scale, parallax_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused projection of the layer input into q, k, v and the probe rho (the
+ * probe is a learned projection of the input: blog "Parallax: Breaking the
+ * Boundary Bias with Parameterized Local Linear Attention", "The Core
+ * Insight: Covariance Correction" and "Architecture-Optimizer Codesign", the
+ * W_R projection; paper page "Parallax: Parameterized Local Linear Attention
+ * for Language Modeling", "Abstract").
+ *   x        [B, T, d_model] bf16, row b T + t (device)
+ *   w        [(2 H_q + 2 H_kv) d, d_model] bf16: the rows of W_Q (H_q d),
+ *            W_K (H_kv d), W_V (H_kv d) and W_R (H_q d), each output
+ *            feature's weights contiguous (device)
+ *   q, rho   [B, H_q, T, d] bf16 outputs (device)
+ *   k_cache, v_cache  [B, H_kv, S_max, d] bf16 (device): row past_lens[b] + t
+ *            of sequence b receives token t (rows at or past S_max are not
+ *            written); other rows are left as they are
+ *   past_lens [B] device int32 or NULL (all 0), clamped to [0, S_max]
+ * Each output is the fp32-accumulated dot product rounded to bf16 (nearest
+ * even). d_model must be a positive multiple of 64; d in {64, 128};
+ * T <= S_max; all tensor pointers 16-byte aligned. Host checks precede the
+ * single launch on `stream`; nothing is allocated. Errors: NULL_POINTER,
+ * BAD_SHAPE (non-positive sizes, T > S_max, d_model not a multiple of 64),
+ * UNSUPPORTED (d not 64/128, sizes past 32-bit offsets), MISALIGNED, HIP. */
+parallax_status_t parallax_qkvr_projection(const void* x, const void* w, void* q, void* rho,
+                                           void* k_cache, void* v_cache,
+                                           const int32_t* past_lens, int B, int T, int d_model,
+                                           int H_q, int H_kv, int d, int S_max, void* stream);
 
 #ifdef __cplusplus
 }

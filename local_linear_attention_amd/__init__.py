@@ -23,6 +23,7 @@ __all__ = [
     "ParallaxError", "lib", "library_path", "abi_version", "status_string", "decode_plan",
     "decode_workspace_size", "decode", "decode_partial", "decode_combine", "prefill",
     "prefill_chunked", "prefill_train", "prefill_backward_workspace_size", "prefill_backward",
+    "qkvr_projection",
     "STATUS", "EXPORTED_SYMBOLS",
 ]
 
@@ -45,7 +46,7 @@ EXPORTED_SYMBOLS = (
     "parallax_decode_workspace_size", "parallax_decode", "parallax_decode_partial",
     "parallax_decode_combine", "parallax_prefill", "parallax_prefill_chunked",
     "parallax_prefill_train", "parallax_prefill_backward_workspace_size",
-    "parallax_prefill_backward",
+    "parallax_prefill_backward", "parallax_qkvr_projection",
 )
 
 
@@ -103,6 +104,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.parallax_prefill_backward_workspace_size.argtypes = [i, i, i, i]
     L.parallax_prefill_backward.restype = i
     L.parallax_prefill_backward.argtypes = [vp] * 13 + [i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.parallax_qkvr_projection.restype = i
+    L.parallax_qkvr_projection.argtypes = [vp] * 7 + [i] * 7 + [vp]
     return L
 
 
@@ -343,3 +346,43 @@ def prefill_backward(q, rho, k, v, seq_lens, out, mu_v, stats, dout, scale: floa
             float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes,
             _stream_ptr(q.device)), "parallax_prefill_backward")
     return dq, drho, dk, dv
+
+
+def qkvr_projection(x, w, H_q: int, H_kv: int, d: int, *, k_cache=None, v_cache=None,
+                    past_lens=None, S_max: int | None = None):
+    """Fused projection of x [B, T, d_model] (bf16) by the packed weight
+    w [(2 H_q + 2 H_kv) d, d_model] (rows of W_Q, W_K, W_V, W_R).
+
+    Returns (q, k_cache, v_cache, rho): q, rho [B, H_q, T, d] bf16; k and v
+    written into rows past_lens[b] + t of the caches [B, H_kv, S_max, d]
+    (allocated, zero-filled, with S_max = T when not given). See
+    parallax_qkvr_projection.
+    """
+    _dev_tensor(x, "x")
+    _dev_tensor(w, "w")
+    if x.dim() != 3 or w.dim() != 2 or w.shape[1] != x.shape[2] or \
+            w.shape[0] != (2 * H_q + 2 * H_kv) * d:
+        raise ValueError("x is [B, T, d_model] and w [(2 H_q + 2 H_kv) d, d_model]")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bf16")
+    B, T, d_model = x.shape
+    if k_cache is None:
+        S = T if S_max is None else int(S_max)
+        k_cache = torch.zeros((B, H_kv, S, d), dtype=torch.bfloat16, device=x.device)
+        v_cache = torch.zeros_like(k_cache)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name)
+        if t.shape[:2] != (B, H_kv) or t.shape[3] != d or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16 [B, H_kv, S_max, d]")
+    if past_lens is not None:
+        _dev_tensor(past_lens, "past_lens")
+        if past_lens.dtype != torch.int32 or past_lens.shape != (B,):
+            raise ValueError("past_lens must be int32 [B]")
+    q = torch.empty((B, H_q, T, d), dtype=torch.bfloat16, device=x.device)
+    rho = torch.empty_like(q)
+    with torch.cuda.device(x.device):
+        _check(lib().parallax_qkvr_projection(
+            x.data_ptr(), w.data_ptr(), q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), 0 if past_lens is None else past_lens.data_ptr(), B, T, d_model,
+            H_q, H_kv, d, k_cache.shape[2], _stream_ptr(x.device)), "parallax_qkvr_projection")
+    return q, k_cache, v_cache, rho

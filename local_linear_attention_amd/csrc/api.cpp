@@ -404,3 +404,32 @@ parallax_status_t parallax_prefill_backward(
 }
 
 }  // extern "C"
+
+extern "C" {
+
+parallax_status_t parallax_qkvr_projection(const void* x, const void* w, void* q, void* rho,
+                                           void* k_cache, void* v_cache,
+                                           const int32_t* past_lens, int B, int T, int d_model,
+                                           int H_q, int H_kv, int d, int S_max, void* stream) {
+  try {
+    if (!x || !w || !q || !rho || !k_cache || !v_cache) return PARALLAX_ERR_NULL_POINTER;
+    if (B <= 0 || T <= 0 || d_model <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || S_max <= 0 ||
+        T > S_max || d_model % 64 != 0)
+      return PARALLAX_ERR_BAD_SHAPE;
+    if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
+    const long long N = (2LL * H_q + 2LL * H_kv) * d;
+    if ((long long)B * T >= (1LL << 31) / 2 || 128LL * d_model * 2 >= (1LL << 31) ||
+        N >= (1LL << 31) / 2 || (long long)B * T / 128 >= 65535)
+      return PARALLAX_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(q) || !aligned16(rho) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(past_lens) & 3u))
+      return PARALLAX_ERR_MISALIGNED;
+    parallax::ProjArgs a{x, w, q, k_cache, v_cache, rho, past_lens, B, T, d_model, H_q, H_kv, d,
+                         S_max};
+    return hip_status(parallax::launch_projection(a, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+}  // extern "C"

@@ -58,9 +58,23 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// Fused q, k, v, rho projection of x [B T, d_model] by the packed weight
+// W [(2 H_q + 2 H_kv) d, d_model] (rows W_Q, W_K, W_V, W_R).
+struct ProjArgs {
+  const void* x;
+  const void* w;
+  void* q;
+  void* k;
+  void* v;
+  void* rho;
+  const int32_t* past_lens;  // k, v rows written at past_lens[b] + t (null: 0)
+  int B, T, d_model, H_q, H_kv, d, S_max;
+};
+
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st);
+hipError_t launch_projection(const ProjArgs& a, hipStream_t st);
 
 }  // namespace parallax

@@ -34,7 +34,9 @@ replaces (conjugate gradient for the probe), pinned in
 ``tests/test_lla_oracle_pins.py``; ``lla_contrast`` measures its accuracy and
 cost against softmax attention on synthetic data. ``parallax_grad_oracle``
 gives the gradients of the causal prefill (fp64 autograd of the explicit
-definition), pinned in ``tests/test_grad_oracle_pins.py``.
+definition), pinned in ``tests/test_grad_oracle_pins.py``; ``projection_oracle``
+gives the fused q, k, v, rho projection, pinned in
+``tests/test_projection_oracle_pins.py``.
 """
 
 from .parallax_oracle import (  # noqa: F401
@@ -49,3 +51,4 @@ from .parallax_oracle import (  # noqa: F401
     oracle_chunk_full,
 )
 from .parallax_grad_oracle import oracle_prefill_grads  # noqa: F401
+from .projection_oracle import oracle_qkvr_projection  # noqa: F401

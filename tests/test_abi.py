@@ -38,7 +38,7 @@ def header_functions():
 
 def test_header_symbols_exported(L):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(pa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -220,3 +220,18 @@ def test_prefill_backward_argument_errors(L):
     assert _bwd(L, ws=P + 4) == MISAL
     need = L.parallax_prefill_backward_workspace_size(1, 2, 256, 128)
     assert _bwd(L, ws_bytes=need - 1) == WS
+
+
+def _proj(L, x=P, w=P, q=P, rho=P, k=P, v=P, past=0, B=2, T=64, C=256, Hq=4, Hkv=2, d=128, S=64):
+    return L.parallax_qkvr_projection(x, w, q, rho, k, v, past, B, T, C, Hq, Hkv, d, S, None)
+
+
+def test_projection_argument_errors(L):
+    assert _proj(L, x=0) == NULLP
+    assert _proj(L, v=0) == NULLP
+    assert _proj(L, T=0) == SHAPE
+    assert _proj(L, T=65, S=64) == SHAPE
+    assert _proj(L, C=96) == SHAPE          # d_model not a multiple of 64
+    assert _proj(L, d=96) == UNSUP
+    assert _proj(L, w=P + 8) == MISAL
+    assert _proj(L, past=P + 2) == MISAL
