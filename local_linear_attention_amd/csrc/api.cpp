@@ -107,7 +107,7 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   if (G > 4 && G % 4 != 0) return PARALLAX_ERR_UNSUPPORTED;
   const long long esz = dtype == PARALLAX_F32 ? 4 : 2;
   if (((long long)S_max + 64) * d * esz >= (1LL << 31)) return PARALLAX_ERR_UNSUPPORTED;
-  if ((long long)H_kv * ((G + 3) / 4) > 65535 || B > 65535) return PARALLAX_ERR_UNSUPPORTED;
+  if (B > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y
   if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;  // NaN scale
   if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
@@ -115,6 +115,7 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   int ns = 0, chunk = 0;
   parallax_status_t st = plan(B, H_q, H_kv, S_max, num_splits, &ns, &chunk);
   if (st != PARALLAX_OK) return st;
+  if (ns > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid z
   const bool direct = (ns == 1);
   if ((direct || need_out) && !out) return PARALLAX_ERR_NULL_POINTER;
   if (out && !aligned16(out)) return PARALLAX_ERR_MISALIGNED;

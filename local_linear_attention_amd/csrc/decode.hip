@@ -189,11 +189,18 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   __shared__ float lds_state[kWaves][4][4];          // m, l, bs, cref per head
   __shared__ float lds_vec[kWaves][2][4][D];         // A, C per head
 
-  const int split = blockIdx.x;
+  // Grid (KV head x head group, sequence, split): workgroups are dealt to
+  // the 8 XCDs in linear order (x fastest), so every XCD gets the same
+  // splits of a different set of streams (with 8 KV heads: one head of every
+  // sequence), whatever the split count. With the split varying fastest, a
+  // power-of-two split count put split s of every stream on one XCD, and the
+  // mostly empty high splits of a ragged batch left some XCDs with far more
+  // work than others.
   const int ngroups = (G + 3) / 4;
-  const int hk = blockIdx.y / ngroups;
-  const int hgrp = blockIdx.y % ngroups;
-  const int b = blockIdx.z;
+  const int hk = blockIdx.x / ngroups;
+  const int hgrp = blockIdx.x % ngroups;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int Gw = min(4, G - 4 * hgrp);               // heads in this workgroup
   const int h0 = hk * G + 4 * hgrp;                  // first query head
 
@@ -481,7 +488,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const int32_t* __res
 template <typename T, int D>
 hipError_t launch_partial_t(const DecodeArgs& a, hipStream_t st) {
   const int ngroups = (a.G + 3) / 4;
-  dim3 grid(a.num_splits, a.H_kv * ngroups, a.B);
+  dim3 grid(a.H_kv * ngroups, a.B, a.num_splits);  // stream fastest in the linear order
   hipLaunchKernelGGL((decode_partial_kernel<T, D>), grid, dim3(256), 0, st,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.rho),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.seq_lens, a.out,
