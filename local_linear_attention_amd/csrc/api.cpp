@@ -56,17 +56,23 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
     const int cus = cu_count();
     if (cus <= 0) return PARALLAX_ERR_HIP;
     // About two workgroups per compute unit over the padded key range, with
-    // chunks of 512..2048 keys (one 4-wave workgroup per CU already saturates
-    // HBM on this access pattern; the cap keeps ragged batches balanced), but
-    // at most 32 splits per stream, since the fused merge reads every split's
-    // record and its cost grows with the split count.
+    // chunks of 128..2048 keys (the cap keeps ragged batches balanced), at
+    // most 32 splits per stream (the fused merge reads every split's record),
+    // and at most 16 splits when the chunks come out shorter than 512 keys:
+    // there each workgroup streams for so short a time that the merge's
+    // record reads decide, while a few more splits still cut the latency of
+    // small batches (one 1024-key sequence: 2 splits 11.0 us, 8 splits 7.5 us).
     const long long target = 2LL * cus;
     long long want = ((long long)S_max * streams + target - 1) / target;
     chunk = round_up(want, kChunkQuantum);
-    if (chunk < 512) chunk = 512;
+    if (chunk < kChunkQuantum) chunk = kChunkQuantum;
     if (chunk > 2048) chunk = 2048;
     const int min_chunk = round_up((S_max + kMaxAutoSplits - 1) / kMaxAutoSplits, kChunkQuantum);
     if (chunk < min_chunk) chunk = min_chunk;
+    if (chunk < 512) {
+      const int min_small = round_up((S_max + 15) / 16, kChunkQuantum);
+      if (chunk < min_small) chunk = min_small;
+    }
   }
   if (chunk > full) chunk = full;
   const int ns = (S_max + chunk - 1) / chunk;
