@@ -72,10 +72,8 @@ __device__ __forceinline__ void prefill_rows(
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ past_lens, float* __restrict__ out, float* __restrict__ mu_out,
     float4* __restrict__ stats, int H_q, int H_kv, int G, int T, int S_max, float scale_log2, int rb,
-    char (&kv_lds)[2][2][Pre<D>::TILE]) {
+    int h, int b, char (&kv_lds)[2][2][Pre<D>::TILE]) {
   using P = Pre<D>;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int hk = h / G;
   // Row t of this chunk sits at position past + t of the sequence and sees
   // keys 0 .. past + t of the cache; rows t >= n are zero.
@@ -388,13 +386,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     float4* __restrict__ stats, int H_q, int H_kv, int G, int T, int S_max, float scale_log2) {
   __shared__ __attribute__((aligned(16))) char kv_lds[2][2][Pre<D>::TILE];  // [buffer][K, V]
   const int nrb = (T + kRows - 1) / kRows;
-  const int x = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs in linear order. Remap so that each
+  // XCD takes a contiguous range of (sequence, head, row-block pair) tiles:
+  // the query heads of one KV head are adjacent, so the workgroups running at
+  // the same time on an XCD mostly share one K/V slice in that XCD's L2.
+  const unsigned npairs = gridDim.x;
+  const unsigned total = gridDim.x * gridDim.y * gridDim.z;
+  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const unsigned L = total % 8u == 0u ? (lin % 8u) * (total / 8u) + lin / 8u : lin;
+  const int x = (int)(L % npairs);
+  const int h = (int)((L / npairs) % (unsigned)H_q);
+  const int b = (int)(L / (npairs * (unsigned)H_q));
   prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
-                  scale_log2, nrb - 1 - x, kv_lds);
+                  scale_log2, nrb - 1 - x, h, b, kv_lds);
   if (x != nrb - 1 - x) {
     __syncthreads();
     prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
-                    scale_log2, x, kv_lds);
+                    scale_log2, x, h, b, kv_lds);
   }
 }
 
