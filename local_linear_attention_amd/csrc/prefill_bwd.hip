@@ -113,6 +113,19 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Workgroups are dealt to the 8 XCDs in linear order; this remaps the
+// linear index so that each XCD takes a contiguous range of (x, y, z) tiles
+// (x fastest), whose neighbours share their K/V or q/rho/dO rows in that
+// XCD's L2. Returns the remapped x, y, z.
+__device__ __forceinline__ void xcd_tile(int& x, int& y, int& z) {
+  const unsigned total = gridDim.x * gridDim.y * gridDim.z;
+  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const unsigned L = total % 8u == 0u ? (lin % 8u) * (total / 8u) + lin / 8u : lin;
+  x = (int)(L % gridDim.x);
+  y = (int)((L / gridDim.x) % gridDim.y);
+  z = (int)(L / (gridDim.x * gridDim.y));
+}
+
 __device__ __forceinline__ bf16x8 load8(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
 }
@@ -164,10 +177,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 // ---------------------------------------------------------------------------
 // 2. dq, drho: one row block (128 rows from rb * 128) of one (b, h).
 template <int D>
-__device__ __forceinline__ void dq_rows(const BwdArgs& a, int rb, char (&lds)[2][2][Bw<D>::TILE]) {
+__device__ __forceinline__ void dq_rows(const BwdArgs& a, int rb, int h, int b,
+                                        char (&lds)[2][2][Bw<D>::TILE]) {
   using P = Bw<D>;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int hk = h / a.G;
   const int T = a.T;
   const int n = min(max(a.seq_lens[b], 0), T);
@@ -364,11 +376,12 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][2][Bw<D>::TILE];  // [buffer][K, V]
   const int nrb = (a.T + kQRows - 1) / kQRows;
-  const int x = blockIdx.x;
-  dq_rows<D>(a, nrb - 1 - x, lds);
+  int x, h, b;
+  xcd_tile(x, h, b);
+  dq_rows<D>(a, nrb - 1 - x, h, b, lds);
   if (x != nrb - 1 - x) {
     __syncthreads();
-    dq_rows<D>(a, x, lds);
+    dq_rows<D>(a, x, h, b, lds);
   }
 }
 
@@ -379,11 +392,9 @@ struct RowStat {
 };
 
 template <int D>
-__device__ __forceinline__ void dkv_keys(const BwdArgs& a, int kb, char (&lds)[2][4][Bw<D>::TILE],
-                                         RowStat (&rst)[2][kKRows]) {
+__device__ __forceinline__ void dkv_keys(const BwdArgs& a, int kb, int hk, int b,
+                                         char (&lds)[2][4][Bw<D>::TILE], RowStat (&rst)[2][kKRows]) {
   using P = Bw<D>;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
   const int G = a.G;
   const int T = a.T;
   const int n = min(max(a.seq_lens[b], 0), T);
@@ -591,11 +602,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][4][Bw<D>::TILE];  // [buffer][q, rho, dO hi, dO lo]
   __shared__ RowStat rst[2][kKRows];
   const int nkb = (a.S_max + kKKeys - 1) / kKKeys;
-  const int x = blockIdx.x;
-  dkv_keys<D>(a, x, lds, rst);  // early (heavy) key block
+  int x, hk, b;
+  xcd_tile(x, hk, b);
+  dkv_keys<D>(a, x, hk, b, lds, rst);  // early (heavy) key block
   if (x != nkb - 1 - x) {
     __syncthreads();
-    dkv_keys<D>(a, nkb - 1 - x, lds, rst);
+    dkv_keys<D>(a, nkb - 1 - x, hk, b, lds, rst);
   }
 }
 
