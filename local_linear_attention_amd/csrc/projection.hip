@@ -45,8 +45,25 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   const int c = lane & 15;
   const int wf = wave >> 1;  // feature half of the tile
   const int wx = wave & 1;   // token half of the tile
-  const int F0 = blockIdx.x * kTileF;
-  const int X0 = blockIdx.y * kTileX;
+  // Tile order. Workgroups are dealt to the 8 XCDs in linear order: remap so
+  // each XCD takes a contiguous range, and walk that range in groups of 8 x 8
+  // (token, feature) tiles, so the ~64 workgroups an XCD runs at once share
+  // 8 token tiles of x and 8 feature tiles of W in its L2 instead of all
+  // feature tiles of W (when the tile counts are multiples of 8).
+  int ft = blockIdx.x, xt = blockIdx.y;
+  {
+    const unsigned nf = gridDim.x, nx = gridDim.y, total = nf * nx;
+    if (nf % 8u == 0u && nx % 8u == 0u) {
+      const unsigned lin = blockIdx.x + nf * blockIdx.y;
+      const unsigned L = (lin % 8u) * (total / 8u) + lin / 8u;
+      const unsigned st = L / 64u, w = L % 64u;  // 8 x 8 super-tile, position in it
+      const unsigned sf = nf / 8u;
+      ft = (int)(8u * (st % sf) + w % 8u);
+      xt = (int)(8u * (st / sf) + w / 8u);
+    }
+  }
+  const int F0 = ft * kTileF;
+  const int X0 = xt * kTileX;
   const int M = a.B * a.T;
   const int N = (2 * a.H_q + 2 * a.H_kv) * a.d;
   const int KB = a.d_model * 2;  // bytes per row of x and W
