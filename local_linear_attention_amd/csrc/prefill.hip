@@ -390,13 +390,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   // XCD takes a contiguous range of (sequence, head, row-block pair) tiles:
   // the query heads of one KV head are adjacent, so the workgroups running at
   // the same time on an XCD mostly share one K/V slice in that XCD's L2.
-  const unsigned npairs = gridDim.x;
-  const unsigned total = gridDim.x * gridDim.y * gridDim.z;
-  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const unsigned L = total % 8u == 0u ? (lin % 8u) * (total / 8u) + lin / 8u : lin;
-  const int x = (int)(L % npairs);
-  const int h = (int)((L / npairs) % (unsigned)H_q);
-  const int b = (int)(L / (npairs * (unsigned)H_q));
+  int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const unsigned long long total = (unsigned long long)gridDim.x * gridDim.y * gridDim.z;
+  if (total < (1ull << 31) && total % 8u == 0u) {
+    const unsigned npairs = gridDim.x, tot = (unsigned)total;
+    const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const unsigned L = (lin % 8u) * (tot / 8u) + lin / 8u;
+    x = (int)(L % npairs);
+    h = (int)((L / npairs) % gridDim.y);
+    b = (int)(L / (npairs * gridDim.y));
+  }
   prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
                   scale_log2, nrb - 1 - x, h, b, kv_lds);
   if (x != nrb - 1 - x) {

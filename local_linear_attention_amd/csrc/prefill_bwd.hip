@@ -118,12 +118,18 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 // (x fastest), whose neighbours share their K/V or q/rho/dO rows in that
 // XCD's L2. Returns the remapped x, y, z.
 __device__ __forceinline__ void xcd_tile(int& x, int& y, int& z) {
-  const unsigned total = gridDim.x * gridDim.y * gridDim.z;
-  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const unsigned L = total % 8u == 0u ? (lin % 8u) * (total / 8u) + lin / 8u : lin;
-  x = (int)(L % gridDim.x);
-  y = (int)((L / gridDim.x) % gridDim.y);
-  z = (int)(L / (gridDim.x * gridDim.y));
+  x = blockIdx.x;
+  y = blockIdx.y;
+  z = blockIdx.z;
+  const unsigned long long total = (unsigned long long)gridDim.x * gridDim.y * gridDim.z;
+  if (total < (1ull << 31) && total % 8u == 0u) {
+    const unsigned tot = (unsigned)total;
+    const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const unsigned L = (lin % 8u) * (tot / 8u) + lin / 8u;
+    x = (int)(L % gridDim.x);
+    y = (int)((L / gridDim.x) % gridDim.y);
+    z = (int)(L / (gridDim.x * gridDim.y));
+  }
 }
 
 __device__ __forceinline__ bf16x8 load8(const char* p) {

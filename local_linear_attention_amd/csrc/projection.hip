@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   // feature tiles of W (when the tile counts are multiples of 8).
   int ft = blockIdx.x, xt = blockIdx.y;
   {
-    const unsigned nf = gridDim.x, nx = gridDim.y, total = nf * nx;
+    const unsigned nf = gridDim.x, nx = gridDim.y, total = nf * nx;  // < 2^31: host-checked
     if (nf % 8u == 0u && nx % 8u == 0u) {
       const unsigned lin = blockIdx.x + nf * blockIdx.y;
       const unsigned L = (lin % 8u) * (total / 8u) + lin / 8u;
