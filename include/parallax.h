@@ -1,5 +1,7 @@
 /*
- * parallax.h - C ABI of libparallax, the MI355X (gfx950) Parallax forward pass.
+ * parallax.h - C ABI of libparallax: the MI355X (gfx950) Parallax attention
+ * (decode, causal prefill, chunked prefill, the prefill backward) and the
+ * fused q, k, v, rho projection that feeds it.
  *
  * Parallax ("Parallax: Parameterized Local Linear Attention for Language
  * Modeling", paper page, "Abstract"; explainer blog "Parallax: Breaking the
@@ -28,9 +30,12 @@
  *    frees memory, never synchronises, and keeps no mutable global state (a
  *    lazily filled, thread-safe cache of per-device compute-unit counts is the
  *    only global).
- *  - Inputs are read only. `out` is written in full (every element).
- *  - `dtype` is the storage type of q, rho, K and V (bf16 or fp32); all
- *    accumulation is fp32 and `out` is always fp32.
+ *  - Inputs are read only. Outputs are written in full (every element), except
+ *    the K/V caches of parallax_qkvr_projection, of which only the projected
+ *    rows are written.
+ *  - `dtype` is the storage type of q, rho, K and V (bf16 or fp32; fp32 for
+ *    decode only); all accumulation is fp32 and attention outputs and
+ *    gradients are fp32.
  *  - `seq_lens` is a device int32 array [B]. Its values cannot be checked on
  *    the host without a synchronisation, so kernels clamp them to [0, S_max]
  *    (for prefill, rows t >= seq_lens[b] are written as zeros). Keys at or past
