@@ -65,7 +65,7 @@ extern "C" {
 typedef enum {
   PARALLAX_OK = 0,
   PARALLAX_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
-  PARALLAX_ERR_BAD_SHAPE = 2,    /* a size <= 0, H_q % H_kv != 0, T > S_max, ... */
+  PARALLAX_ERR_BAD_SHAPE = 2,    /* a size <= 0, H_q % H_kv != 0, T > S_max, scale not finite, ... */
   PARALLAX_ERR_UNSUPPORTED = 3,  /* d, G, dtype or size outside what is built */
   PARALLAX_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
   PARALLAX_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required */
@@ -116,7 +116,8 @@ size_t parallax_decode_workspace_size(int B, int H_q, int d, int num_splits);
  *   v_cache   [B, H_kv, S_max, d]  dtype
  *   seq_lens  [B]                  int32 (device)
  *   out       [B, H_q, d]          fp32, written in full
- *   scale     softmax scale applied to q . k only (never to rho . k)
+ *   scale     softmax scale applied to q . k only (never to rho . k); any finite
+ *             value (negative and zero included)
  *   num_splits 0 = automatic plan, else the requested split count
  *   workspace  device scratch of at least parallax_decode_workspace_size()
  *              bytes for the resolved plan (may be NULL when that is 0)

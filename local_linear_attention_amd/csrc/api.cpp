@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include "kernels.h"
@@ -114,7 +115,7 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   const long long esz = dtype == PARALLAX_F32 ? 4 : 2;
   if (((long long)S_max + 64) * d * esz >= (1LL << 31)) return PARALLAX_ERR_UNSUPPORTED;
   if (B > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y
-  if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;  // NaN scale
+  if (!std::isfinite(scale)) return PARALLAX_ERR_BAD_SHAPE;  // NaN or infinite scale
   if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return PARALLAX_ERR_MISALIGNED;
@@ -264,7 +265,7 @@ parallax_status_t prefill_common(const void* q, const void* rho, const void* k, 
       ((long long)T + 256) * d * 2 >= (1LL << 31))
     return PARALLAX_ERR_UNSUPPORTED;
   if (B > 65535 || H_q > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y, z limits
-  if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return PARALLAX_ERR_BAD_SHAPE;
   if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
       (reinterpret_cast<uintptr_t>(past_lens) & 3u))
@@ -326,7 +327,7 @@ parallax_status_t check_prefill_shape(int B, int H_q, int H_kv, int d, int T, in
   if (((long long)S_max + 256) * d * 4 >= (1LL << 31) || ((long long)T + 256) * d * 4 >= (1LL << 31))
     return PARALLAX_ERR_UNSUPPORTED;
   if (B > 65535 || H_q > 65535) return PARALLAX_ERR_UNSUPPORTED;
-  if (!(scale == scale)) return PARALLAX_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return PARALLAX_ERR_BAD_SHAPE;
   return PARALLAX_OK;
 }
 

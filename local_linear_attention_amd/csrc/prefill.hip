@@ -195,19 +195,49 @@ __device__ __forceinline__ void prefill_rows(
     // ---- transposed scores: lane (g, c) holds row my_row, keys 16 T + 4 g + i.
     // The rho . k accumulators start at -c (c = rho_t . k_0, known from block
     // 0 on), so they come out already relative to the reference.
+    // Issue order (pinned by scheduling barriers): every K operand read, then
+    // the score MFMAs, then every V operand read, so the V reads are in flight
+    // while the scores finish and the softmax runs, instead of each value
+    // MFMA waiting on its own LDS round trip.
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    bf16x8 kop[2][P::KST];
+#pragma unroll
+    for (int T2 = 0; T2 < 2; ++T2) {
+      const char* krow = &kv_lds[buf][0][(16 * T2 + c) * P::LSTR + 16 * g];
+#pragma unroll
+      for (int kk = 0; kk < P::KST; ++kk)
+        kop[T2][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(krow + 64 * kk));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 sc[2], rc[2];
 #pragma unroll
     for (int T2 = 0; T2 < 2; ++T2) {
       sc[T2] = f32x4{0.f, 0.f, 0.f, 0.f};
       rc[T2] = rinit;
-      const char* krow = &kv_lds[buf][0][(16 * T2 + c) * P::LSTR + 16 * g];
 #pragma unroll
       for (int kk = 0; kk < P::KST; ++kk) {
-        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(krow + 64 * kk));
-        sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc[T2], 0, 0, 0);
-        rc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rop[kk], rc[T2], 0, 0, 0);
+        sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[T2][kk], qop[kk], sc[T2], 0, 0, 0);
+        rc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[T2][kk], rop[kk], rc[T2], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // V operands. The B operand of N-tile j (dims 16 j .. 16 j + 15) in lane
+    // (g, c) is V at dim 16 j + c for key slots e = 0..7 (keys 16 (e / 4) +
+    // 4 g + e % 4). Each half (e < 4, e >= 4) comes from one transposing LDS
+    // load: within a group of 16 lanes, lane 4 a + b receives element b of
+    // the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12, so lane
+    // s of group g addresses key 16 h + 4 g + s / 4 at dims 16 j + 4 (s % 4)
+    // .. + 3.
+    const char* vbase = &kv_lds[buf][1][(4 * g + (c >> 2)) * P::VSTR + 8 * (c & 3)];
+    i16x4 vr[P::DPL][2];
+#pragma unroll
+    for (int j = 0; j < P::DPL; ++j) {
+      vr[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * j));
+      vr[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * j + 16 * P::VSTR));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (kb == 0) {
       const float cref = __shfl(rc[0][0], c);  // key 0 sits in lane (0, c), slot 0
       rinit = f32x4{-cref, -cref, -cref, -cref};
@@ -290,23 +320,10 @@ __device__ __forceinline__ void prefill_rows(
     const bf16x8 a_qh = as_bf16x8(qhw[0], qhw[1], qhw[2], qhw[3]);
     const bf16x8 a_ql = as_bf16x8(qlw[0], qlw[1], qlw[2], qlw[3]);
 
-    // ---- value MFMAs. The B operand of N-tile j (dims 16 j .. 16 j + 15) in
-    // lane (g, c) is V at dim 16 j + c for key slots e = 0..7 (keys
-    // 16 (e / 4) + 4 g + e % 4). Each half (e < 4, e >= 4) comes from one
-    // transposing LDS load: within a group of 16 lanes, lane 4 a + b receives
-    // element b of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and
-    // a + 12, so lane s of group g addresses key 16 h + 4 g + s / 4 at dims
-    // 16 j + 4 (s % 4) .. + 3.
-    const char* vbase = &kv_lds[buf][1][(4 * g + (c >> 2)) * P::VSTR + 8 * (c & 3)];
+    // ---- value MFMAs
 #pragma unroll
     for (int j = 0; j < P::DPL; ++j) {
-      typedef short i16x4 __attribute__((ext_vector_type(4)));
-      typedef short i16x8 __attribute__((ext_vector_type(8)));
-      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * j));
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * j + 16 * P::VSTR));
-      const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vr[j][0], vr[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
       accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ph, vop, accA[j], 0, 0, 0);
       accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pl, vop, accA[j], 0, 0, 0);
       accC[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_qh, vop, accC[j], 0, 0, 0);

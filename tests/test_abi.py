@@ -99,6 +99,7 @@ def test_decode_argument_errors(L, fn):
     assert _decode(L, fn, Hq=3, Hkv=2) == SHAPE
     assert _decode(L, fn, ns=-1) == SHAPE
     assert _decode(L, fn, scale=float("nan")) == SHAPE
+    assert _decode(L, fn, scale=float("inf")) == SHAPE
     assert _decode(L, fn, d=96) == UNSUP
     assert _decode(L, fn, dtype=7) == UNSUP
     assert _decode(L, fn, Hq=6, Hkv=1) == UNSUP  # G = 6: not <= 4 and not a multiple of 4
@@ -142,6 +143,7 @@ def test_prefill_argument_errors(L):
     assert _prefill(L, T=300, S=256) == SHAPE
     assert _prefill(L, Hq=5, Hkv=2) == SHAPE
     assert _prefill(L, scale=float("nan")) == SHAPE
+    assert _prefill(L, scale=-float("inf")) == SHAPE
     assert _prefill(L, dtype=F32) == UNSUP
     assert _prefill(L, d=32) == UNSUP
     assert _prefill(L, q=P + 2) == MISAL

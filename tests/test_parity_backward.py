@@ -33,6 +33,9 @@ def rel_err(got, ref, live=None):
     if not live.any():
         return 0.0
     den = np.abs(ref[live]).max(axis=-1)
+    if den.max() == 0:  # an identically zero gradient (dq at scale 0)
+        assert np.all(got[live] == 0)
+        return 0.0
     den = np.maximum(den, 1e-3 * den.max())
     return float((np.abs(got[live] - ref[live]).max(axis=-1) / den).max())
 
@@ -111,6 +114,12 @@ def test_group_sizes(H_q, H_kv):
 def test_edge_lengths():
     w = replace_shape(WORKLOADS[5], B=4, T=160, H_q=2, H_kv=1)
     check(w, seed=4, lens=[0, 1, 33, 128], S_max=200)
+
+
+@pytest.mark.parametrize("scale", [-128 ** -0.5, 0.0])
+def test_negative_and_zero_scale(scale):
+    w = replace_shape(WORKLOADS[5], B=2, T=200, H_q=4, H_kv=2, scale=scale)
+    check(w, seed=9, lens=[200, 141])
 
 
 def test_large_key_offset():

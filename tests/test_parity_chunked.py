@@ -75,6 +75,11 @@ def test_ragged_past_and_chunk_lengths():
     check(w, past_lens=[300, 0, 41], chunk_lens=[160, 77, 0], S_max=500)
 
 
+@pytest.mark.parametrize("scale", [-128 ** -0.5, 0.0])
+def test_negative_and_zero_scale(scale):
+    check(replace_shape(SMALL, scale=scale))
+
+
 def test_group_sizes_and_head_dim_64():
     check(replace_shape(SMALL, H_q=8, H_kv=2))
     check(replace_shape(SMALL, d=64, q_std=64 ** -0.25, k_std=64 ** -0.25))

@@ -113,6 +113,11 @@ def test_unscaled_dot_reading():
     check(SMALL2, seq_lens=[700, 64, 640], scale_mult=1 / math.sqrt(128))
 
 
+@pytest.mark.parametrize("scale_mult", [-1.0, -8.0, 0.0])
+def test_negative_and_zero_scale(scale_mult):
+    check(SMALL2, seq_lens=[700, 300, 129], scale_mult=scale_mult, num_splits=(0, 1, 5))
+
+
 def test_deterministic_bitwise_static_paths():
     """One split, and the two-phase partial + combine, are bitwise repeatable."""
     w = SMALL2

@@ -97,6 +97,13 @@ def test_unscaled_dot_reading():
     check(replace_shape(SMALL, scale=128 ** -0.5))
 
 
+@pytest.mark.parametrize("scale", [-128 ** -0.5, -4.0, 0.0])
+def test_negative_and_zero_scale(scale):
+    # scale < 0 weights the least similar keys most; scale = 0 is the uniform
+    # average over the causal window (weights 1/(t+1))
+    check(replace_shape(SMALL, scale=scale), seq_lens=[200, 131])
+
+
 def test_large_key_offset():
     # keys with a large common component make rho . k carry a large offset
     w = SMALL
