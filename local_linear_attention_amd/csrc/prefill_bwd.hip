@@ -530,12 +530,28 @@ __device__ __forceinline__ void dkv_keys(const BwdArgs& a, int kb, int hk, int b
 #pragma unroll
       for (int i = 0; i < 4; ++i) rr[T2][i] = -rst[buf][16 * T2 + 4 * g + i].c;
       const int roff = (16 * T2 + c) * P::STR + 16 * g;
+      // Every row read of a pair of tiles (q and rho, then dO high and low)
+      // is issued before the MFMAs that use them (order pinned).
 #pragma unroll
-      for (int kk = 0; kk < P::KST; ++kk) {
-        sc[T2] = mfma(load8(&lds[buf][0][roff + 64 * kk]), kop[kk], sc[T2]);
-        rr[T2] = mfma(load8(&lds[buf][1][roff + 64 * kk]), kop[kk], rr[T2]);
-        gg[T2] = mfma(load8(&lds[buf][2][roff + 64 * kk]), vop[kk], gg[T2]);
-        gg[T2] = mfma(load8(&lds[buf][3][roff + 64 * kk]), vop[kk], gg[T2]);
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 x0[P::KST], x1[P::KST];
+#pragma unroll
+        for (int kk = 0; kk < P::KST; ++kk) {
+          x0[kk] = load8(&lds[buf][2 * half][roff + 64 * kk]);
+          x1[kk] = load8(&lds[buf][2 * half + 1][roff + 64 * kk]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < P::KST; ++kk) {
+          if (half == 0) {
+            sc[T2] = mfma(x0[kk], kop[kk], sc[T2]);
+            rr[T2] = mfma(x1[kk], kop[kk], rr[T2]);
+          } else {
+            gg[T2] = mfma(x0[kk], vop[kk], gg[T2]);
+            gg[T2] = mfma(x1[kk], vop[kk], gg[T2]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     float pv[8], dsv[8], drv[8];
@@ -572,21 +588,24 @@ __device__ __forceinline__ void dkv_keys(const BwdArgs& a, int kb, int hk, int b
     }
   };
 
-  Stage stage[2];
-  auto step = [&](int s, int buf, Stage& next) {
+  // One register stage: step s contracts block s from one LDS buffer, moves
+  // block s + 1 from registers into the other and loads block s + 2 (a step
+  // of contraction covers the load; the second stage's 22 registers are
+  // worth more as early operand reads).
+  Stage stage;
+  auto step = [&](int s, int buf) {
     if (s < S) contract(s, buf);
-    store(buf ^ 1, next);
-    load(s + 3, next);
+    store(buf ^ 1, stage);
+    load(s + 2, stage);
     __syncthreads();
   };
-  load(0, stage[0]);
-  load(1, stage[1]);
-  store(0, stage[0]);
-  load(2, stage[0]);
+  load(0, stage);
+  store(0, stage);
+  load(1, stage);
   __syncthreads();
   for (int s = 0; s < S; s += 2) {
-    step(s, 0, stage[1]);
-    step(s + 1, 1, stage[0]);
+    step(s, 0);
+    step(s + 1, 1);
   }
 
   // accumulator element i of lane (g, c): key kw0 + 4 g + i, dim 16 j + c
