@@ -426,8 +426,9 @@ parallax_status_t parallax_qkvr_projection(const void* x, const void* w, void* q
       return PARALLAX_ERR_BAD_SHAPE;
     if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
     const long long N = (2LL * H_q + 2LL * H_kv) * d;
-    if ((long long)B * T >= (1LL << 31) / 2 || 128LL * d_model * 2 >= (1LL << 31) ||
-        N >= (1LL << 31) / 2 || (long long)B * T / 128 >= 65535)
+    // 32-bit buffer offsets within a 256-row tile; grid y = token tiles of 256
+    if ((long long)B * T >= (1LL << 31) / 2 || 256LL * d_model * 2 >= (1LL << 31) ||
+        N >= (1LL << 31) / 2 || ((long long)B * T + 255) / 256 > 65535)
       return PARALLAX_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(q) || !aligned16(rho) || !aligned16(k_cache) ||
         !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(past_lens) & 3u))

@@ -235,5 +235,7 @@ def test_projection_argument_errors(L):
     assert _proj(L, T=65, S=64) == SHAPE
     assert _proj(L, C=96) == SHAPE          # d_model not a multiple of 64
     assert _proj(L, d=96) == UNSUP
+    assert _proj(L, C=1 << 22) == UNSUP                  # a 256-row tile of x past 32-bit offsets
+    assert _proj(L, B=1, T=65535 * 256 + 1, S=1 << 25) == UNSUP  # more than 65535 token tiles
     assert _proj(L, w=P + 8) == MISAL
     assert _proj(L, past=P + 2) == MISAL
