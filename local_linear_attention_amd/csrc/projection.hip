@@ -84,24 +84,29 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   const int N = (2 * a.H_q + 2 * a.H_kv) * a.d;
   const int KB = a.d_model * 2;  // bytes per row of x and W
 
-  const __amdgpu_buffer_rsrc_t wrs =
-      make_rsrc(static_cast<const __bf16*>(a.w) + (size_t)F0 * a.d_model, (uint32_t)max(0, min(kTileF, N - F0)) * KB);
-  const __amdgpu_buffer_rsrc_t xrs =
-      make_rsrc(static_cast<const __bf16*>(a.x) + (size_t)X0 * a.d_model, (uint32_t)max(0, min(kTileX, M - X0)) * KB);
+  // Byte sizes of the workgroup's W and x rows. The compiler clamps them on
+  // the vector ALU; readfirstlane returns them to scalar registers, or every
+  // buffer load would be wrapped in a loop over the distinct descriptors.
+  const uint32_t wbytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(kTileF, N - F0)) * KB);
+  const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(kTileX, M - X0)) * KB);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(static_cast<const __bf16*>(a.w) + (size_t)F0 * a.d_model, wbytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(static_cast<const __bf16*>(a.x) + (size_t)X0 * a.d_model, xbytes);
 
   // Thread tid's pieces: rows (tid + kThreads i) / 8, 16-byte column
   // (tid + kThreads i) % 8 of the stage. Past d_model the offsets run into
   // the next row (in range, unused) or past the last row (zeros).
+  // The stage offset kt * 128 bytes goes in the scalar offset operand.
   auto load = [&](int kt, i32x4 (&sw)[kPPW], i32x4 (&sx)[kPPX]) {
+    const int soff = __builtin_amdgcn_readfirstlane(kt * kK * 2);
 #pragma unroll
     for (int i = 0; i < kPPW; ++i) {
       const int idx = tid + kThreads * i;
-      sw[i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (uint32_t)(idx / 8) * KB + (uint32_t)kt * kK * 2 + (idx % 8) * 16, 0, 0);
+      sw[i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (uint32_t)(idx / 8) * KB + (idx % 8) * 16, soff, 0);
     }
 #pragma unroll
     for (int i = 0; i < kPPX; ++i) {
       const int idx = tid + kThreads * i;
-      sx[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (uint32_t)(idx / 8) * KB + (uint32_t)kt * kK * 2 + (idx % 8) * 16, 0, 0);
+      sx[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (uint32_t)(idx / 8) * KB + (idx % 8) * 16, soff, 0);
     }
   };
   auto store = [&](int buf, const i32x4 (&sw)[kPPW], const i32x4 (&sx)[kPPX]) {
