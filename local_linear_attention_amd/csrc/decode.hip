@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     float* __restrict__ ws, unsigned* __restrict__ counters, int H_q, int H_kv, int G, int S_max,
     int chunk, int num_splits, float scale_log2) {
   using P = Dec<T, D>;
-  __shared__ float lds_state[kWaves][4][4];          // m, l, bs, cref per head
+  __shared__ __attribute__((aligned(16))) float lds_state[kWaves][4][4];  // m, l, bs, cref per head
   __shared__ float lds_vec[kWaves][2][4][D];         // A, C per head
 
   // Grid (KV head x head group, sequence, split): workgroups are dealt to
@@ -397,33 +397,37 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     else
       *p = v;
   };
+  // Branch-free: every LDS read of the item is issued before any is used
+  // (the states of the 4 waves as one 16-byte read each), waves without keys
+  // (l = 0) get weight 0, and the reference c0 is the first wave's with keys.
   for (int idx = tid; idx < Gw * D; idx += 256) {
     const int h = idx / D;
     const int dim = idx % D;
-    float M = -INFINITY;
-    float c0 = 0.f;
-    bool have = false;
+    float4 st[kWaves];  // m, l, bs, cref
+    float Aw[kWaves], Cw[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (lds_state[w][h][1] > 0.f) {
-        if (!have) c0 = lds_state[w][h][3];
-        have = true;
-        M = fmaxf(M, lds_state[w][h][0]);
-      }
+      st[w] = *reinterpret_cast<const float4*>(&lds_state[w][h][0]);
+      Aw[w] = lds_vec[w][0][h][dim];
+      Cw[w] = lds_vec[w][1][h][dim];
+    }
+    float M = -INFINITY;
+    float c0 = 0.f;
+#pragma unroll
+    for (int w = kWaves - 1; w >= 0; --w) {
+      M = st[w].y > 0.f ? fmaxf(M, st[w].x) : M;
+      c0 = st[w].y > 0.f ? st[w].w : c0;
     }
     float l = 0.f, bs = 0.f, A = 0.f, C = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float lw = lds_state[w][h][1];
-      if (lw > 0.f) {
-        const float al = exp2f(lds_state[w][h][0] - M);
-        const float sh = lds_state[w][h][3] - c0;
-        const float Aw = lds_vec[w][0][h][dim];
-        l += al * lw;
-        bs += al * (lds_state[w][h][2] + sh * lw);
-        A += al * Aw;
-        C += al * (lds_vec[w][1][h][dim] + sh * Aw);
-      }
+      const float lw = st[w].y;
+      const float al = lw > 0.f ? exp2f(st[w].x - M) : 0.f;
+      const float sh = st[w].w - c0;
+      l += al * lw;
+      bs += al * (st[w].z + sh * lw);
+      A += al * Aw[w];
+      C += al * (Cw[w] + sh * Aw[w]);
     }
     if (direct) {
       out[((size_t)b * H_q + h0 + h) * D + dim] = l > 0.f ? (A * (1.f + bs / l) - C) / l : 0.f;
