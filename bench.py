@@ -111,6 +111,33 @@ class DecodeRunner:
              float(inp["scale"]), dcode, self.ns, self.ws.data_ptr(), ws_bytes, self.stream)
             for k, v in zip(ks, vs)]
 
+    def read_probe(self, steps, warmup):
+        """Event-timed seconds per launch of the plain streaming read over the
+        same rotated K and V buffers (the whole caches; used only where every
+        cache row is valid, so it reads exactly the decode's KV bytes)."""
+        torch = self.torch
+        sink = torch.zeros(4096, dtype=torch.int32, device=self.ks[0].device)
+        nbytes = self.ks[0].numel() * self.ks[0].element_size()
+        args = [(k.data_ptr(), v.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), self.stream)
+                for k, v in zip(self.ks, self.vs)]
+
+        def one(i):
+            st = self.L.parallax_read_probe(*args[i % len(args)])
+            if st != 0:
+                raise RuntimeError(f"read probe failed with status {st}")
+
+        for i in range(warmup):
+            one(i)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(steps):
+            one(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps / 1e3
+
     def step(self, i):
         st = self.L.parallax_decode(*self.pargs[i % len(self.pargs)])
         if st != 0:
@@ -432,6 +459,15 @@ def main():
         },
     }
     log(f"{w.name}: {gbs:.0f} GB/s per step, decode kernel {part_gbs:.0f} GB/s")
+    if all(n == w.S_max for n in main_r.lens):
+        read_s = main_r.read_probe(args.steps, args.warmup)
+        read_gbs = main_r.kv_bytes / read_s / 1e9
+        result["read_reference"] = {
+            "kernel": "parallax_read_probe: plain streaming read of the same K and V buffers",
+            "kernel_us": read_s * 1e6, "GB_per_s": round(read_gbs, 1),
+            "pct_of_hbm_peak": round(100 * read_gbs / HBM_PEAK_GBS, 2),
+            "decode_over_read": round(part_gbs / read_gbs, 4)}
+        log(f"plain read of the same bytes: {read_gbs:.0f} GB/s")
 
     workloads = {}
     if args.workloads == "all":

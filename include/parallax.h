@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 3
+#define PARALLAX_ABI_VERSION 4
 
 typedef enum {
   PARALLAX_OK = 0,
@@ -263,6 +263,25 @@ parallax_status_t parallax_qkvr_projection(const void* x, const void* w, void* q
                                            void* k_cache, void* v_cache,
                                            const int32_t* past_lens, int B, int T, int d_model,
                                            int H_q, int H_kv, int d, int S_max, void* stream);
+
+/* Measurement support, not part of the method: a plain streaming read that
+ * serves as the reference for the decode kernel's KV-stream bandwidth. It
+ * reads every 16-byte word of a[0 .. bytes_each) and b[0 .. bytes_each)
+ * exactly once (non-temporal loads, about two workgroups per compute unit,
+ * each streaming one contiguous share) and XORs every 32-bit word of both
+ * into the sink, one workgroup's XOR into word (workgroup mod sink_words):
+ *   a, b        device buffers, 16-byte aligned, read only
+ *   bytes_each  a positive multiple of 16
+ *   sink        device uint32 array of sink_words words; the XOR of all its
+ *               words changes by the XOR of the data (clear it first to get
+ *               the XOR of the data alone)
+ *   sink_words  positive; at least twice the compute-unit count keeps the
+ *               workgroups' atomics on distinct words
+ * One launch on `stream`, nothing allocated. Errors: NULL_POINTER,
+ * BAD_SHAPE (bytes_each not a positive multiple of 16, sink_words <= 0),
+ * MISALIGNED, HIP. */
+parallax_status_t parallax_read_probe(const void* a, const void* b, size_t bytes_each,
+                                      uint32_t* sink, int sink_words, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,9 @@ Functions mirror the C entry points:
 * ``decode_plan``, ``decode_workspace_size``
 * ``decode`` (one shot), ``decode_partial`` + ``decode_combine`` (two phases)
 * ``prefill`` (causal), ``prefill_chunked`` (causal against an existing cache)
+* ``prefill_train`` + ``prefill_backward`` (gradients of the causal prefill)
+* ``qkvr_projection`` (fused q, k, v, rho projection into the attention layouts)
+* ``read_probe`` (measurement support: a plain streaming read of two buffers)
 """
 
 from __future__ import annotations
@@ -23,7 +26,7 @@ __all__ = [
     "ParallaxError", "lib", "library_path", "abi_version", "status_string", "decode_plan",
     "decode_workspace_size", "decode", "decode_partial", "decode_combine", "prefill",
     "prefill_chunked", "prefill_train", "prefill_backward_workspace_size", "prefill_backward",
-    "qkvr_projection",
+    "qkvr_projection", "read_probe",
     "STATUS", "EXPORTED_SYMBOLS",
 ]
 
@@ -46,7 +49,7 @@ EXPORTED_SYMBOLS = (
     "parallax_decode_workspace_size", "parallax_decode", "parallax_decode_partial",
     "parallax_decode_combine", "parallax_prefill", "parallax_prefill_chunked",
     "parallax_prefill_train", "parallax_prefill_backward_workspace_size",
-    "parallax_prefill_backward", "parallax_qkvr_projection",
+    "parallax_prefill_backward", "parallax_qkvr_projection", "parallax_read_probe",
 )
 
 
@@ -106,6 +109,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.parallax_prefill_backward.argtypes = [vp] * 13 + [i, i, i, i, i, i, f, i, vp, sz, vp]
     L.parallax_qkvr_projection.restype = i
     L.parallax_qkvr_projection.argtypes = [vp] * 7 + [i] * 7 + [vp]
+    L.parallax_read_probe.restype = i
+    L.parallax_read_probe.argtypes = [vp, vp, ctypes.c_size_t, vp, i, vp]
     return L
 
 
@@ -386,3 +391,19 @@ def qkvr_projection(x, w, H_q: int, H_kv: int, d: int, *, k_cache=None, v_cache=
             v_cache.data_ptr(), 0 if past_lens is None else past_lens.data_ptr(), B, T, d_model,
             H_q, H_kv, d, k_cache.shape[2], _stream_ptr(x.device)), "parallax_qkvr_projection")
     return q, k_cache, v_cache, rho
+
+
+def read_probe(a, b, sink):
+    """Measurement support: reads every byte of the same-sized device tensors
+    a and b once and XORs their 32-bit words into the words of sink (a device
+    int32 tensor); the XOR of all of sink's words changes by the XOR of the
+    data. See parallax_read_probe."""
+    _dev_tensor(a, "a")
+    _dev_tensor(b, "b")
+    _dev_tensor(sink, "sink")
+    nbytes = a.numel() * a.element_size()
+    if b.numel() * b.element_size() != nbytes or sink.dtype != torch.int32:
+        raise ValueError("a and b must hold the same number of bytes; sink is int32")
+    with torch.cuda.device(a.device):
+        _check(lib().parallax_read_probe(a.data_ptr(), b.data_ptr(), nbytes, sink.data_ptr(),
+                                         sink.numel(), _stream_ptr(a.device)), "parallax_read_probe")

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libparallax.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill_bwd.hip", "projection.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill_bwd.hip", "projection.hip", "read_probe.hip"]
 
 
 def hipcc() -> str:

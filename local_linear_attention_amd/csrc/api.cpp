@@ -442,3 +442,23 @@ parallax_status_t parallax_qkvr_projection(const void* x, const void* w, void* q
 }
 
 }  // extern "C"
+
+extern "C" {
+
+parallax_status_t parallax_read_probe(const void* a, const void* b, size_t bytes_each,
+                                      uint32_t* sink, int sink_words, void* stream) {
+  try {
+    if (!a || !b || !sink) return PARALLAX_ERR_NULL_POINTER;
+    if (bytes_each == 0 || bytes_each % 16 != 0 || sink_words <= 0) return PARALLAX_ERR_BAD_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+      return PARALLAX_ERR_MISALIGNED;
+    const int cus = cu_count();
+    if (cus <= 0) return PARALLAX_ERR_HIP;
+    return hip_status(parallax::launch_read_probe(a, b, bytes_each, sink, (unsigned)sink_words,
+                                                  2 * cus, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+}  // extern "C"

@@ -24,12 +24,14 @@
 //
 // Work layout. A workgroup of 4 waves owns one (b, KV head, group of <= 4
 // query heads, key range of `chunk` keys). Each wave takes every 4th block
-// of 32 keys. Per block a lane loads its K and V pieces straight from HBM into
+// of 32 keys. Per block a lane loads its K and V pieces from HBM into
 // registers with range-checked buffer loads (rows at or past the sequence
-// length come back as zeros, so padding is never read). V rows, read in whole
-// 256-byte rows per instruction, carry the non-temporal streaming hint; K is
-// read as 64-byte pieces of 16 rows per instruction, whose two halves of each
-// 128-byte line must meet in L2, so K keeps the default policy. Two MFMA
+// length come back as zeros, so padding is never read). Both are read in
+// whole rows per instruction and carry the non-temporal streaming hint. V
+// needs no rearranging; for bf16 the wave passes its K block through a
+// private LDS region to form the score MFMA's operand (16 rows x 64 bytes per
+// MFMA). Loading that operand straight from HBM fetched half of each 128-byte
+// line per instruction and could not take the hint: 2-5% slower. Two MFMA
 // contractions do the arithmetic:
 //   scores:  [32 keys x d] x [d x 16 probe columns] with v_mfma_f32_16x16x32_bf16,
 //            probe column 4h+t holds q_h for t in {0,1} and rho_h for t in {2,3},
@@ -71,6 +73,9 @@ struct Dec {
   static constexpr int VW = DPL * ESZ / 4;              // words per V row piece
   static constexpr bool F32 = (ESZ == 4);
   static constexpr int REC = 2 * D + 4;                 // fp32 words per partial record
+  static constexpr int RP = ROWB / 16;                  // 16-byte pieces per K/V row
+  static constexpr int KSTR = ROWB + 16;                // LDS row stride of a staged K block (bf16)
+  static constexpr int KLDS = F32 ? 16 : kBlockKeys * KSTR;  // bytes of one wave's K block
 };
 
 // 8 consecutive elements (one MFMA operand) from words; fp32 gives hi and lo.
@@ -188,6 +193,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   using P = Dec<T, D>;
   __shared__ __attribute__((aligned(16))) float lds_state[kWaves][4][4];  // m, l, bs, cref per head
   __shared__ float lds_vec[kWaves][2][4][D];         // A, C per head
+  __shared__ __attribute__((aligned(16))) char k_lds[kWaves][P::KLDS];  // bf16: each wave's K block
 
   // Grid (KV head x head group, sequence, split): workgroups are dealt to
   // the 8 XCDs in linear order (x fastest), so every XCD gets the same
@@ -255,13 +261,24 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   bool first = true;
 
   // K pieces for the score MFMA and V rows for the value MFMA of one block.
+  // bf16: K is read in whole rows (piece i of lane l is 16-byte piece
+  // l + 64 i of the block, row-major), with the streaming hint like V, and
+  // rearranged through this wave's LDS region; fp32: each lane reads its
+  // operand pieces (16 rows x 64 bytes per instruction) directly.
   auto load_block = [&](int blk, Words<P::KW> (&kw)[2][P::KSTEPS], Words<P::VW> (&vw)[8]) {
 #pragma unroll
     for (int T2 = 0; T2 < 2; ++T2)
 #pragma unroll
-      for (int kk = 0; kk < P::KSTEPS; ++kk)
-        kw[T2][kk] = buffer_load<P::KW>(
-            krs, (uint32_t)(blk + 16 * T2 + c) * P::ROWB + (32 * kk + 8 * g) * P::ESZ);
+      for (int kk = 0; kk < P::KSTEPS; ++kk) {
+        if constexpr (!P::F32) {
+          const int pc = lane + 64 * (T2 * P::KSTEPS + kk);
+          kw[T2][kk] = buffer_load<P::KW, kNontemporal>(
+              krs, (uint32_t)(blk + pc / P::RP) * P::ROWB + (pc % P::RP) * 16);
+        } else {
+          kw[T2][kk] = buffer_load<P::KW>(
+              krs, (uint32_t)(blk + 16 * T2 + c) * P::ROWB + (32 * kk + 8 * g) * P::ESZ);
+        }
+      }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       vw[e] = buffer_load<P::VW, kNontemporal>(
@@ -273,6 +290,28 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     Words<P::VW> vw[8];
     load_block(blk, kw, vw);
 
+    // bf16: the block's K rows into this wave's LDS region (rows padded by
+    // 16 bytes), then the A operand of each score MFMA (key row 16 T2 + c,
+    // dims 32 kk + 8 g .. + 7) read back. A wave's LDS accesses take effect in
+    // order, so no barrier is needed.
+    bf16x8 kop[2][P::KSTEPS];
+    if constexpr (!P::F32) {
+      char* kl = k_lds[wave];
+#pragma unroll
+      for (int T2 = 0; T2 < 2; ++T2)
+#pragma unroll
+        for (int kk = 0; kk < P::KSTEPS; ++kk) {
+          const int pc = lane + 64 * (T2 * P::KSTEPS + kk);
+          *reinterpret_cast<i32x4*>(kl + (pc / P::RP) * P::KSTR + (pc % P::RP) * 16) =
+              __builtin_bit_cast(i32x4, kw[T2][kk]);
+        }
+#pragma unroll
+      for (int T2 = 0; T2 < 2; ++T2)
+#pragma unroll
+        for (int kk = 0; kk < P::KSTEPS; ++kk)
+          kop[T2][kk] = *reinterpret_cast<const bf16x8*>(kl + (16 * T2 + c) * P::KSTR + 64 * kk + 16 * g);
+    }
+
     // ---- scores: lane (g, c) gets probe column c for keys 16 T2 + 4 g + i
     f32x4 sc[2];
 #pragma unroll
@@ -281,7 +320,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
       for (int kk = 0; kk < P::KSTEPS; ++kk) {
         bf16x8 khi, klo;
-        to_operand<T>(kw[T2][kk].w, khi, klo);
+        if constexpr (!P::F32)
+          khi = kop[T2][kk];
+        else
+          to_operand<T>(kw[T2][kk].w, khi, klo);
         sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_hi[kk], sc[T2], 0, 0, 0);
         if constexpr (P::F32) {
           sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_lo[kk], sc[T2], 0, 0, 0);

@@ -76,5 +76,7 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st);
 hipError_t launch_projection(const ProjArgs& a, hipStream_t st);
+hipError_t launch_read_probe(const void* a, const void* b, size_t bytes_each, uint32_t* sink,
+                             unsigned sink_words, int workgroups, hipStream_t st);
 
 }  // namespace parallax

@@ -38,7 +38,7 @@ def header_functions():
 
 def test_header_symbols_exported(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert set(names) == set(pa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -239,3 +239,14 @@ def test_projection_argument_errors(L):
     assert _proj(L, B=1, T=65535 * 256 + 1, S=1 << 25) == UNSUP  # more than 65535 token tiles
     assert _proj(L, w=P + 8) == MISAL
     assert _proj(L, past=P + 2) == MISAL
+
+
+def test_read_probe_argument_errors(L):
+    f = L.parallax_read_probe
+    assert f(0, P, 1 << 20, P, 512, None) == NULLP
+    assert f(P, P, 1 << 20, 0, 512, None) == NULLP
+    assert f(P, P, 0, P, 512, None) == SHAPE
+    assert f(P, P, (1 << 20) + 8, P, 512, None) == SHAPE  # not a multiple of 16
+    assert f(P, P, 1 << 20, P, 0, None) == SHAPE
+    assert f(P + 8, P, 1 << 20, P, 512, None) == MISAL
+    assert f(P, P, 1 << 20, P + 2, 512, None) == MISAL
