@@ -56,14 +56,16 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
   } else {
     const int cus = cu_count();
     if (cus <= 0) return PARALLAX_ERR_HIP;
-    // About two workgroups per compute unit over the padded key range, with
-    // chunks of 128..2048 keys (the cap keeps ragged batches balanced), at
-    // most 32 splits per stream (the fused merge reads every split's record),
-    // and at most 16 splits when the chunks come out shorter than 512 keys:
-    // there each workgroup streams for so short a time that the merge's
-    // record reads decide, while a few more splits still cut the latency of
-    // small batches (one 1024-key sequence: 2 splits 11.0 us, 8 splits 7.5 us).
-    const long long target = 2LL * cus;
+    // About one workgroup per compute unit over the padded key range (a
+    // second workgroup on a compute unit trails the first: gqa-decode, 8 x 4096
+    // keys, takes 25.4 us at 4 splits against 26.3 at 8), with chunks of
+    // 128..2048 keys (the cap keeps ragged batches balanced), at most 32 splits
+    // per stream (the fused merge reads every split's record), and at most 16
+    // splits when the chunks come out shorter than 512 keys: there each
+    // workgroup streams for so short a time that the merge's record reads
+    // decide, while a few more splits still cut the latency of small batches
+    // (one 1024-key sequence: 2 splits 11.0 us, 8 splits 7.5 us).
+    const long long target = (long long)cus;
     long long want = ((long long)S_max * streams + target - 1) / target;
     chunk = round_up(want, kChunkQuantum);
     if (chunk < kChunkQuantum) chunk = kChunkQuantum;
