@@ -67,6 +67,7 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
     // (one 1024-key sequence: 2 splits 11.0 us, 8 splits 7.5 us).
     const long long target = (long long)cus;
     long long want = ((long long)S_max * streams + target - 1) / target;
+    if (want > 2048) want = 2048;  // the cap below, applied before the narrowing to int
     chunk = round_up(want, kChunkQuantum);
     if (chunk < kChunkQuantum) chunk = kChunkQuantum;
     if (chunk > 2048) chunk = 2048;

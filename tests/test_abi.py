@@ -104,6 +104,7 @@ def test_decode_argument_errors(L, fn):
     assert _decode(L, fn, dtype=7) == UNSUP
     assert _decode(L, fn, Hq=6, Hkv=1) == UNSUP  # G = 6: not <= 4 and not a multiple of 4
     assert _decode(L, fn, S=1 << 24) == UNSUP    # a (b, h_kv) slice of 4 GiB
+    assert _decode(L, fn, S=(1 << 23) - 64) == UNSUP  # (S + 64) d 2 bytes reaches 2^31
     assert _decode(L, fn, k=P + 8) == MISAL
     assert _decode(L, fn, lens=P + 2) == MISAL
     assert _decode(L, fn, ws=0) == WS

@@ -224,3 +224,28 @@ def test_fused_workspace_reuse_counters_return_to_zero():
         assert rel_err(out.cpu().numpy(), oracle_all(cpu)) < TOL
         ctr = ws[rec_words:].view(torch.int32)
         assert int(ctr.abs().sum()) == 0
+
+
+@pytest.mark.slow
+def test_longest_cache_accepted():
+    """The longest KV cache the ABI accepts, (S_max + 64) d * 2 bytes just under 2^31
+    per (b, KV head) for bf16, d = 128: the last rows' byte offsets sit next to 2^31.
+    The sequence ends 5 keys before S_max (NaN padding after it). Automatic plan,
+    and one workgroup per head group streaming all of it."""
+    d = 128
+    S = (1 << 31) // (d * 2) - 64 - 1
+    n = S - 5
+    w = replace_shape(WORKLOADS[2], B=1, H_q=2, H_kv=1, S_max=S)
+    print(f"[decode parity] longest cache S_max={S} n={n}", flush=True)
+    dev = make_decode_inputs(w, device="cuda", seq_lens=[n])
+    outs = {ns: run_decode(dev, ns) for ns in (0, 1)}
+    K = oracle.parallax_oracle._f64(dev["k_cache"][0, 0, :n].cpu())
+    V = oracle.parallax_oracle._f64(dev["v_cache"][0, 0, :n].cpu())
+    for h in range(2):
+        ref = oracle.parallax_attend(oracle.parallax_oracle._f64(dev["q"][0, h].cpu()),
+                                     oracle.parallax_oracle._f64(dev["rho"][0, h].cpu()),
+                                     K, V, dev["scale"])
+        errs = {ns: rel_err(o[0, h][None], ref[None]) for ns, o in outs.items()}
+        print(f"   head {h}: max rel err {errs}", flush=True)
+        assert max(errs.values()) < TOL
+
