@@ -130,3 +130,28 @@ def test_chunk_workload_full_size_sampled():
     err = max(rel_err(got[b, h, t][None], o[None]) for (b, h, t), o in ex.items())
     print(f"   {len(rows)} sampled rows: {err:.3e}", flush=True)
     assert err < TOL
+
+
+@pytest.mark.slow
+def test_longest_cache_accepted():
+    """A 40-row chunk at the end of the longest cache the ABI accepts for prefill,
+    (S_max + 256) d * 2 bytes just under 2^31 (d = 128): the chunk's keys sit at
+    byte offsets next to 2^31. The sequence ends 3 rows before S_max; rows 40..47
+    of the 48-row query tensor lie past the chunk and must be zero."""
+    d = 128
+    S = (1 << 31) // (d * 2) - 256 - 1
+    past = S - 40 - 3
+    w = replace_shape(CHUNK_WORKLOAD, B=1, T=48, past=past, H_q=2, H_kv=1)
+    print(f"[chunked parity] longest cache S_max={S} past={past}", flush=True)
+    dev = make_chunk_inputs(w, device="cuda", chunk_lens=[40], S_max=S)
+    got = run(dev)
+    assert np.isfinite(got).all()
+    assert not got[0, :, 40:].any()
+    cpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dev.items()}
+    rows = [(0, 0, 0), (0, 1, 39)]
+    ex = oracle.oracle_chunk_rows(cpu["q"], cpu["rho"], cpu["k_cache"], cpu["v_cache"],
+                                  cpu["past_lens"], cpu["chunk_lens"], cpu["scale"], rows)
+    err = max(rel_err(got[b, h, t][None], o[None]) for (b, h, t), o in ex.items())
+    print(f"   sampled rows {rows}: {err:.3e}", flush=True)
+    assert err < TOL
+
