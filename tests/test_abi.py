@@ -159,6 +159,16 @@ def test_python_binding_rejects_cpu_tensors():
         pa.decode(t, t, t[None], t[None], torch.ones(1, dtype=torch.int32), 1.0)
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback path: without the built library every entry point raises."""
+    monkeypatch.setattr(pa, "_LIB_PATH", str(tmp_path / "libparallax.so"))
+    monkeypatch.setattr(pa, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        pa.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        pa.decode_plan(1, 2, 1, 128, 2)
+
+
 def test_prefill_chunked_argument_errors(L):
     f = L.parallax_prefill_chunked
 
