@@ -55,6 +55,38 @@ def check(w, **kw):
 SMALL = replace_shape(CHUNK_WORKLOAD, B=2, T=160, past=300, H_q=4, H_kv=2)
 
 
+def _random_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        G = int(rng.choice([1, 2, 4, 8]))
+        H_kv = int(rng.integers(1, 3))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.integers(1, 200))
+        B = int(rng.integers(1, 4))
+        past = [int(x) for x in rng.integers(0, 600, B)]
+        lens = [int(x) for x in rng.integers(0, T + 1, B)]
+        # usually room for the chunk; sometimes a cache that cuts it short
+        S = max(p + t for p, t in zip(past, lens))
+        if rng.random() < 0.4:
+            S -= int(rng.integers(1, 40))
+        else:
+            S += int(rng.integers(0, 50))
+        S = max(S, T, 1)  # the chunk's query rows fit the cache (T <= S_max)
+        cases.append((B, G, H_kv, d, T, S, past, lens))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(8, 2026), ids=lambda c: f"B{c[0]}G{c[1]}Hkv{c[2]}d{c[3]}T{c[4]}S{c[5]}")
+def test_random_shapes(case):
+    """Seeded random shapes: past lengths, chunk lengths (zero included), group
+    sizes, head dims, and caches that cut a chunk short (lengths clamped)."""
+    B, G, H_kv, d, T, S, past, lens = case
+    w = replace_shape(CHUNK_WORKLOAD, B=B, T=T, past=0, H_q=G * H_kv, H_kv=H_kv, d=d,
+                      q_std=d ** -0.25, k_std=d ** -0.25)
+    check(w, past_lens=past, chunk_lens=lens, S_max=S)
+
+
 def test_small_chunk():
     check(SMALL)
 

@@ -94,6 +94,32 @@ def test_head_dims_and_dtypes(d, dtype):
     check(w, seq_lens=[400, 259], num_splits=(0, 1, 3))
 
 
+def _random_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        G = int(rng.choice([1, 2, 3, 4, 8, 12]))
+        H_kv = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+        S = int(rng.integers(1, 1500))
+        B = int(rng.integers(1, 5))
+        lens = [int(x) for x in rng.integers(0, S + 1, B)]
+        splits = (0, 1, int(rng.integers(2, 8)))
+        cases.append((B, G, H_kv, d, dtype, S, lens, splits))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(10, 2024), ids=lambda c: f"B{c[0]}G{c[1]}Hkv{c[2]}d{c[3]}S{c[5]}")
+def test_random_shapes(case):
+    """Seeded random shapes: group sizes, head dims, dtypes, cache lengths,
+    ragged lengths (zero included) and split counts together."""
+    B, G, H_kv, d, dtype, S, lens, splits = case
+    w = replace_shape(WORKLOADS[2], B=B, H_q=G * H_kv, H_kv=H_kv, d=d, S_max=S, dtype=dtype,
+                      q_std=d ** -0.25, k_std=d ** -0.25)
+    check(w, seq_lens=lens, num_splits=splits)
+
+
 def test_rho_zero_is_softmax_attention():
     w = replace_shape(SMALL2, rho_std=0.0)
     check(w, seq_lens=[700, 5, 400])

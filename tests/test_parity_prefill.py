@@ -55,6 +55,31 @@ def check(w, *, seed=0, seq_lens=None, S_max=None, **kw):
 SMALL = replace_shape(WORKLOADS[5], B=2, T=200, H_q=4, H_kv=2)
 
 
+def _random_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        H_kv = int(rng.integers(1, 3))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.integers(1, 400))
+        S = T + int(rng.integers(0, 3)) * int(rng.integers(0, 100))
+        B = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(0, T + 1, B)]
+        cases.append((B, G, H_kv, d, T, S, lens))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(8, 2025), ids=lambda c: f"B{c[0]}G{c[1]}Hkv{c[2]}d{c[3]}T{c[4]}S{c[5]}")
+def test_random_shapes(case):
+    """Seeded random shapes: group sizes, head dims, lengths (zero included),
+    T not a multiple of any tile, and caches longer than T."""
+    B, G, H_kv, d, T, S, lens = case
+    w = replace_shape(WORKLOADS[5], B=B, T=T, H_q=G * H_kv, H_kv=H_kv, d=d,
+                      q_std=d ** -0.25, k_std=d ** -0.25)
+    check(w, seq_lens=lens, S_max=S)
+
+
 def test_small_ragged_tail():
     check(SMALL, seq_lens=[200, 150])
 
