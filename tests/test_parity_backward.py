@@ -122,6 +122,31 @@ def test_negative_and_zero_scale(scale):
     check(w, seed=9, lens=[200, 141])
 
 
+def _random_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        G = int(rng.choice([1, 2, 4, 8]))
+        H_kv = int(rng.integers(1, 3))
+        d = int(rng.choice([64, 128]))
+        T = int(rng.integers(1, 260))
+        S = T + int(rng.integers(0, 2)) * int(rng.integers(1, 90))
+        B = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(0, T + 1, B)]
+        cases.append((B, G, H_kv, d, T, S, lens))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(6, 2027), ids=lambda c: f"B{c[0]}G{c[1]}Hkv{c[2]}d{c[3]}T{c[4]}S{c[5]}")
+def test_random_shapes(case):
+    """Seeded random shapes: group sizes, head dims, lengths (zero included),
+    T not a multiple of any block, and caches longer than T."""
+    B, G, H_kv, d, T, S, lens = case
+    w = replace_shape(WORKLOADS[5], B=B, T=T, H_q=G * H_kv, H_kv=H_kv, d=d,
+                      q_std=d ** -0.25, k_std=d ** -0.25)
+    check(w, seed=11, lens=lens, S_max=S)
+
+
 def test_large_key_offset():
     w = replace_shape(WORKLOADS[5], B=1, T=256, H_q=2, H_kv=1)
     check(w, seed=5, k_offset=4.0)
