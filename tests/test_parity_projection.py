@@ -41,13 +41,24 @@ def _ulp_check(got, ref, absref):
     return frac
 
 
+def _random_shapes(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        H_kv = int(rng.integers(1, 4))
+        H_q = H_kv * int(rng.choice([1, 2, 4]))
+        out.append((int(rng.integers(1, 4)), int(rng.integers(1, 600)), 64 * int(rng.integers(1, 17)),
+                    H_q, H_kv, int(rng.choice([64, 128]))))
+    return out
+
+
 @pytest.mark.parametrize("B,T,C,H_q,H_kv,d", [
     (2, 200, 256, 4, 2, 128),   # ragged token tile, GQA
     (1, 64, 128, 2, 2, 64),     # d = 64
     (3, 130, 512, 6, 2, 64),    # three KV heads' worth of odd sizes
     (2, 77, 192, 2, 1, 64),     # odd number of 64-wide d_model stages; a partial feature tile
     (1, 300, 64, 1, 1, 128),    # one stage; two token tiles, the second ragged
-])
+] + _random_shapes(5, 2028))
 def test_projection_small(B, T, C, H_q, H_kv, d):
     print(f"[projection parity] B={B} T={T} d_model={C} Hq={H_q} Hkv={H_kv} d={d}", flush=True)
     x, w = _inputs(B, T, C, H_q, H_kv, d, seed=B * 1000 + T)
