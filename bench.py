@@ -15,7 +15,8 @@ the launch stream around the timed region, divided by K, gives the kernel's
 average launch duration for the `roofline` object. The other workloads (single-head fp32, ragged batch,
 128K-context split-KV decode, causal prefill) are timed the same way, briefly,
 and reported under "workloads", with a chunked prefill (1024 new rows after
-3072 cached tokens). The `cpu_baseline` leg times the fp64 oracle
+3072 cached tokens), the GQA decode shape at 64 query heads on 8 KV heads, and
+multi-token decode (2 and 4 new tokens per sequence at the GQA decode shape). The `cpu_baseline` leg times the fp64 oracle
 on a bounded sample of the same GQA decode workload on the host cores.
 
 One JSON line is printed at the end.
@@ -321,6 +322,56 @@ def bench_chunked(w, steps, warmup, seed=None):
             "shape": dict(B=w.B, T=w.T, past=w.past, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
 
 
+def bench_tokens(T, steps, warmup, seed=None):
+    """Multi-token decode (parallax_decode_tokens) at the GQA decode shape: T new
+    tokens per sequence after 4096 - T cached ones, 8 rotated cache copies. The
+    algorithmic bytes are the KV stream read once, as for the decode."""
+    import torch
+
+    import local_linear_attention_amd as pa
+    from workloads import CHUNK_WORKLOAD, make_chunk_inputs, replace_shape
+
+    w = replace_shape(CHUNK_WORKLOAD, name=f"multi-token-decode-T{T}", B=8, T=T, past=4096 - T,
+                      H_q=16, H_kv=8, d=128)
+    dev = torch.device("cuda:0")
+    inp = make_chunk_inputs(w, seed=seed, device=dev)
+    S_max = inp["k_cache"].shape[2]
+    caches = [(inp["k_cache"], inp["v_cache"])]
+    for _ in range(7):
+        caches.append((inp["k_cache"].clone(), inp["v_cache"].clone()))
+    ns, chunk = pa.decode_plan(w.B, w.H_q * T, w.H_kv, S_max, 0)
+    ws_bytes = max(pa.decode_workspace_size(w.B, w.H_q * T, w.d, ns), 16)
+    ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device=dev)
+    out = torch.empty((w.B, w.H_q, T, w.d), dtype=torch.float32, device=dev)
+    L = pa.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = [(inp["q"].data_ptr(), inp["rho"].data_ptr(), k.data_ptr(), v.data_ptr(),
+             inp["past_lens"].data_ptr(), inp["chunk_lens"].data_ptr(), out.data_ptr(), w.B,
+             w.H_q, w.H_kv, w.d, T, S_max, float(inp["scale"]), 0, ns, ws.data_ptr(), ws_bytes,
+             stream) for k, v in caches]
+
+    def one(i):
+        if L.parallax_decode_tokens(*args[i % len(args)]) != 0:
+            raise RuntimeError("multi-token decode failed")
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        one(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    kern = ev0.elapsed_time(ev1) / steps / 1e3
+    kv_bytes = w.B * w.H_kv * S_max * w.d * 2 * 2
+    return {"kernel_us": kern * 1e6, "kv_bytes": kv_bytes, "GB_per_s": kv_bytes / kern / 1e9,
+            "pct_of_hbm_peak": 100 * kv_bytes / kern / 1e9 / HBM_PEAK_GBS,
+            "num_splits": ns, "chunk": chunk,
+            "shape": dict(B=w.B, H_q=w.H_q, H_kv=w.H_kv, d=w.d, new_tokens=T, cached=w.past)}
+
+
 def cpu_baseline(runner, min_s=10.0, budget_s=30.0):
     """Times the fp64 oracle on a bounded sample of the GQA decode workload.
 
@@ -394,7 +445,7 @@ def main():
 
     import torch
 
-    from workloads import CHUNK_WORKLOAD, WORKLOADS
+    from workloads import CHUNK_WORKLOAD, WORKLOADS, replace_shape
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -484,6 +535,20 @@ def main():
                 "num_splits": r.ns, "chunk": r.chunk, "steps": ksteps,
                 "dtype": "f32" if idx == 1 else "bf16"}
             del r
+            torch.cuda.empty_cache()
+        wg8 = replace_shape(WORKLOADS[2], name="gqa8-decode", H_q=64)
+        log(f"workload {wg8.name}")
+        r = DecodeRunner(wg8, nbuf=8)
+        s, p = r.run(args.steps, max(3, args.warmup // 4))
+        workloads[wg8.name] = {
+            "us_per_step": s * 1e6, "kernel_us": p * 1e6, "kv_bytes": r.kv_bytes,
+            "GB_per_s": r.kv_bytes / p / 1e9, "pct_of_hbm_peak": 100 * r.kv_bytes / p / 1e9 / HBM_PEAK_GBS,
+            "num_splits": r.ns, "chunk": r.chunk, "shape": dict(B=8, H_q=64, H_kv=8, d=128, kv_len=4096)}
+        del r
+        torch.cuda.empty_cache()
+        for T in (2, 4):
+            log(f"workload multi-token-decode T={T}")
+            workloads[f"multi-token-decode-T{T}"] = bench_tokens(T, args.steps, max(3, args.warmup // 4))
             torch.cuda.empty_cache()
         log("workload causal-prefill")
         workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10)

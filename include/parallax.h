@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 4
+#define PARALLAX_ABI_VERSION 5
 
 typedef enum {
   PARALLAX_OK = 0,
@@ -195,6 +195,33 @@ parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const
                                            const int32_t* chunk_lens, float* out, int B, int H_q,
                                            int H_kv, int d, int T, int S_max, float scale,
                                            parallax_dtype_t dtype, void* stream);
+
+/*
+ * Multi-token decode: the result of parallax_prefill_chunked (same arguments,
+ * layouts and clamping of past_lens and chunk_lens), computed by the split-KV
+ * decode kernel for the few new tokens per sequence of speculative decoding.
+ * Each (query head, token) pair is one decode query: token t of sequence b
+ * attends keys 0 .. past_lens[b] + t, rows t >= chunk_lens[b] are written as
+ * 0, and every KV head is streamed once per group of 4 (query head, token)
+ * pairs. Passage: the same as parallax_decode (one pass over the KV stream,
+ * [blog] "Hardware Efficiency"), with the causal reading of the chunk.
+ *   dtype       PARALLAX_BF16 or PARALLAX_F32
+ *   num_splits, workspace, workspace_bytes as parallax_decode, for
+ *               H_q * T queries: the plan is parallax_decode_plan(B, H_q * T,
+ *               H_kv, S_max, num_splits) and the size
+ *               parallax_decode_workspace_size(B, H_q * T, d, num_splits);
+ *               the same zeroed-counter rule applies.
+ * Limits: (H_q / H_kv) * T must be at most 4 or a multiple of 4
+ * (PARALLAX_ERR_UNSUPPORTED otherwise). Other errors as parallax_decode, plus
+ * PARALLAX_ERR_NULL_POINTER for a NULL past_lens or chunk_lens and
+ * PARALLAX_ERR_BAD_SHAPE for T <= 0 or T > S_max.
+ */
+parallax_status_t parallax_decode_tokens(const void* q, const void* rho, const void* k_cache,
+                                         const void* v_cache, const int32_t* past_lens,
+                                         const int32_t* chunk_lens, float* out, int B, int H_q,
+                                         int H_kv, int d, int T, int S_max, float scale,
+                                         parallax_dtype_t dtype, int num_splits,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal prefill for training: parallax_prefill plus what the backward
  * needs. Besides `out` it writes

@@ -10,6 +10,7 @@ Functions mirror the C entry points:
 * ``decode_plan``, ``decode_workspace_size``
 * ``decode`` (one shot), ``decode_partial`` + ``decode_combine`` (two phases)
 * ``prefill`` (causal), ``prefill_chunked`` (causal against an existing cache)
+* ``decode_tokens`` (the chunked result for a few new tokens, by the split-KV decode)
 * ``prefill_train`` + ``prefill_backward`` (gradients of the causal prefill)
 * ``qkvr_projection`` (fused q, k, v, rho projection into the attention layouts)
 * ``read_probe`` (measurement support: a plain streaming read of two buffers)
@@ -25,7 +26,8 @@ import torch
 __all__ = [
     "ParallaxError", "lib", "library_path", "abi_version", "status_string", "decode_plan",
     "decode_workspace_size", "decode", "decode_partial", "decode_combine", "prefill",
-    "prefill_chunked", "prefill_train", "prefill_backward_workspace_size", "prefill_backward",
+    "prefill_chunked", "decode_tokens", "prefill_train", "prefill_backward_workspace_size",
+    "prefill_backward",
     "qkvr_projection", "read_probe",
     "STATUS", "EXPORTED_SYMBOLS",
 ]
@@ -48,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "parallax_abi_version", "parallax_status_string", "parallax_decode_plan",
     "parallax_decode_workspace_size", "parallax_decode", "parallax_decode_partial",
     "parallax_decode_combine", "parallax_prefill", "parallax_prefill_chunked",
+    "parallax_decode_tokens",
     "parallax_prefill_train", "parallax_prefill_backward_workspace_size",
     "parallax_prefill_backward", "parallax_qkvr_projection", "parallax_read_probe",
 )
@@ -101,6 +104,9 @@ def load_library(path: str) -> ctypes.CDLL:
     L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.parallax_prefill_chunked.restype = i
     L.parallax_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.parallax_decode_tokens.restype = i
+    L.parallax_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
+                                         vp, sz, vp]
     L.parallax_prefill_train.restype = i
     L.parallax_prefill_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.parallax_prefill_backward_workspace_size.restype = sz
@@ -251,12 +257,7 @@ def prefill(q, rho, k, v, seq_lens, scale: float, *, out=None):
     return out
 
 
-def prefill_chunked(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: float, *, out=None):
-    """Chunked causal prefill: row t attends keys 0..past_lens[b] + t of the cache.
-
-    The cache must already hold the chunk's keys and values (see
-    parallax_prefill_chunked). Returns out [B, H_q, T, d] fp32.
-    """
+def _chunk_shapes(q, rho, k_cache, v_cache, past_lens, chunk_lens):
     for name, t in (("q", q), ("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("past_lens", past_lens), ("chunk_lens", chunk_lens)):
         _dev_tensor(t, name)
@@ -272,6 +273,16 @@ def prefill_chunked(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: floa
     for name, t in (("past_lens", past_lens), ("chunk_lens", chunk_lens)):
         if t.dtype != torch.int32 or t.shape != (B,):
             raise ValueError(f"{name} must be int32 [B]")
+    return B, H_q, T, H_kv, d, S_max
+
+
+def prefill_chunked(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: float, *, out=None):
+    """Chunked causal prefill: row t attends keys 0..past_lens[b] + t of the cache.
+
+    The cache must already hold the chunk's keys and values (see
+    parallax_prefill_chunked). Returns out [B, H_q, T, d] fp32.
+    """
+    B, H_q, T, H_kv, d, S_max = _chunk_shapes(q, rho, k_cache, v_cache, past_lens, chunk_lens)
     if out is None:
         out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
@@ -279,6 +290,24 @@ def prefill_chunked(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: floa
             q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             past_lens.data_ptr(), chunk_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, T, S_max,
             float(scale), _dtype_code(q), _stream_ptr(q.device)), "parallax_prefill_chunked")
+    return out
+
+
+def decode_tokens(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: float, *,
+                  num_splits: int = 0, out=None, workspace=None):
+    """Multi-token decode: prefill_chunked's result for a few new tokens per
+    sequence, by the split-KV decode kernel (see parallax_decode_tokens).
+    Returns out [B, H_q, T, d] fp32."""
+    B, H_q, T, H_kv, d, S_max = _chunk_shapes(q, rho, k_cache, v_cache, past_lens, chunk_lens)
+    if out is None:
+        out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    ws, ws_bytes = _workspace(B, H_q * T, H_kv, d, S_max, num_splits, workspace, q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_decode_tokens(
+            q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            past_lens.data_ptr(), chunk_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, T, S_max,
+            float(scale), _dtype_code(q), int(num_splits), ws.data_ptr(), ws_bytes,
+            _stream_ptr(q.device)), "parallax_decode_tokens")
     return out
 
 

@@ -138,8 +138,8 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   void* counters = nullptr;
   if (need > 0 && need_out)
     counters = static_cast<char*>(ws) + records_bytes(B, H_q, d, ns);
-  c->a = parallax::DecodeArgs{q, rho, k, v, seq_lens, out, ws, counters, B, H_q, H_kv, G,
-                              d, S_max, ns, chunk, scale, dtype == PARALLAX_F32};
+  c->a = parallax::DecodeArgs{q, rho, k, v, seq_lens, nullptr, out, ws, counters, B, H_q, H_kv,
+                              G, d, S_max, ns, chunk, 1, scale, dtype == PARALLAX_F32};
   return PARALLAX_OK;
 }
 
@@ -244,6 +244,32 @@ parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_
                                         workspace_bytes, &c);
     if (st != PARALLAX_OK) return st;
     // one launch: with several splits the last workgroup of each stream merges
+    return hip_status(parallax::launch_decode_partial(c.a, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+parallax_status_t parallax_decode_tokens(const void* q, const void* rho, const void* k_cache,
+                                         const void* v_cache, const int32_t* past_lens,
+                                         const int32_t* chunk_lens, float* out, int B, int H_q,
+                                         int H_kv, int d, int T, int S_max, float scale,
+                                         parallax_dtype_t dtype, int num_splits,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!past_lens) return PARALLAX_ERR_NULL_POINTER;
+    if (T <= 0 || H_q <= 0 || H_kv <= 0 || S_max <= 0 || T > S_max || H_q % H_kv != 0)
+      return PARALLAX_ERR_BAD_SHAPE;
+    if ((long long)H_q * T > INT_MAX / 2) return PARALLAX_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(past_lens) & 3u) return PARALLAX_ERR_MISALIGNED;
+    // every (head, token) pair is one query of the decode kernel
+    Checked c;
+    parallax_status_t st = check_decode(q, rho, k_cache, v_cache, chunk_lens, out, true, B,
+                                        H_q * T, H_kv, d, S_max, scale, dtype, num_splits,
+                                        workspace, workspace_bytes, &c);
+    if (st != PARALLAX_OK) return st;
+    c.a.past_lens = past_lens;
+    c.a.ntok = T;
     return hip_status(parallax::launch_decode_partial(c.a, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return PARALLAX_ERR_HIP;

@@ -11,12 +11,14 @@ struct DecodeArgs {
   const void* rho;
   const void* k;
   const void* v;
-  const int32_t* seq_lens;
+  const int32_t* seq_lens;   // key counts, or chunk lengths with past_lens
+  const int32_t* past_lens;  // several tokens per sequence: cached lengths; else null
   float* out;
   void* ws;        // partial records [B, H_q, num_splits, 2d + 4] fp32
   void* counters;  // arrival counters (fused merge), or null for the two-phase form
   int B, H_q, H_kv, G, d, S_max;
   int num_splits, chunk;
+  int ntok;  // tokens per sequence (H_q and G above count (head, token) pairs)
   float scale;
   bool f32;
 };

@@ -38,7 +38,7 @@ def header_functions():
 
 def test_header_symbols_exported(L):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert set(names) == set(pa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -157,6 +157,26 @@ def test_python_binding_rejects_cpu_tensors():
     t = torch.zeros(1, 1, 64)
     with pytest.raises(ValueError):
         pa.decode(t, t, t[None], t[None], torch.ones(1, dtype=torch.int32), 1.0)
+
+
+def _tokens(L, q=P, rho=P, k=P, v=P, past=P, clen=P, out=P, B=2, Hq=4, Hkv=2, d=128, T=2,
+            S=512, scale=1.0, dtype=BF16, ns=2, ws=P, ws_bytes=1 << 30):
+    return L.parallax_decode_tokens(q, rho, k, v, past, clen, out, B, Hq, Hkv, d, T, S, scale,
+                                    dtype, ns, ws, ws_bytes, None)
+
+
+def test_decode_tokens_argument_errors(L):
+    assert _tokens(L, past=0) == NULLP
+    assert _tokens(L, clen=0) == NULLP
+    assert _tokens(L, out=0) == NULLP
+    assert _tokens(L, T=0) == SHAPE
+    assert _tokens(L, T=513) == SHAPE             # more tokens than cache rows
+    assert _tokens(L, Hq=3, Hkv=2) == SHAPE       # H_q not a multiple of H_kv
+    assert _tokens(L, Hq=2, Hkv=1, T=3) == UNSUP  # 6 (head, token) pairs per KV head
+    assert _tokens(L, d=96) == UNSUP
+    assert _tokens(L, past=P + 2) == MISAL
+    assert _tokens(L, ws_bytes=16) == WS
+    assert _tokens(L, scale=float("nan")) == SHAPE
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

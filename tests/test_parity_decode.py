@@ -120,6 +120,14 @@ def test_random_shapes(case):
     check(w, seq_lens=lens, num_splits=splits)
 
 
+def test_head_groups_placed_together():
+    """G = 8 and 12 take two and three head groups per KV head, whose workgroups
+    are placed on one XCD (grid sizes divisible by 8 x groups)."""
+    for G in (8, 12):
+        w = replace_shape(WORKLOADS[2], B=4, H_q=G * 4, H_kv=4, S_max=1024)
+        check(w, seq_lens=[1024, 1000, 517, 3], num_splits=(0, 2, 4))
+
+
 def test_rho_zero_is_softmax_attention():
     w = replace_shape(SMALL2, rho_std=0.0)
     check(w, seq_lens=[700, 5, 400])
