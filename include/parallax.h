@@ -202,8 +202,8 @@ parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const
  * decode kernel for the few new tokens per sequence of speculative decoding.
  * Each (query head, token) pair is one decode query: token t of sequence b
  * attends keys 0 .. past_lens[b] + t, rows t >= chunk_lens[b] are written as
- * 0, and every KV head is streamed once per group of 4 (query head, token)
- * pairs. Passage: the same as parallax_decode (one pass over the KV stream,
+ * 0, and every KV head is streamed once per group of 8 (query head, token)
+ * pairs (of 4 when there are at most 4). Passage: the same as parallax_decode (one pass over the KV stream,
  * [blog] "Hardware Efficiency"), with the causal reading of the chunk.
  *   dtype       PARALLAX_BF16 or PARALLAX_F32
  *   num_splits, workspace, workspace_bytes as parallax_decode, for

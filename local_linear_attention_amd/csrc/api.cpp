@@ -47,7 +47,8 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || S_max <= 0 || H_q % H_kv != 0)
     return PARALLAX_ERR_BAD_SHAPE;
   const int G = H_q / H_kv;
-  const long long groups = (G + 3) / 4;
+  const int hw = parallax::decode_heads_per_workgroup(G);
+  const long long groups = (G + hw - 1) / hw;
   const long long streams = (long long)B * H_kv * groups;
   const int full = round_up(S_max, kChunkQuantum);
   int chunk;

@@ -23,7 +23,8 @@
 // (c_j - c) as above, an associative and commutative merge.
 //
 // Work layout. A workgroup of 4 waves owns one (b, KV head, group of <= 4
-// query heads, key range of `chunk` keys). Each wave takes every 4th block
+// query heads, or <= 8 when the KV head has more than 4, key range of
+// `chunk` keys). Each wave takes every 4th block
 // of 32 keys. Per block a lane loads its K and V pieces from HBM into
 // registers with range-checked buffer loads (rows at or past the sequence
 // length come back as zeros, so padding is never read). Both are read in
@@ -191,7 +192,7 @@ __device__ __forceinline__ f32x2 merge_records(const float* __restrict__ base, i
 // sequence with past p and chunk length c sees keys 0 .. p + t (none when
 // t >= c). Without MT, seq_lens holds the key counts and every head sees
 // them all.
-template <typename T, int D, bool MT>
+template <typename T, int D, bool MT, int HG>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ rho, const T* __restrict__ kc,
     const T* __restrict__ vc, const int32_t* __restrict__ seq_lens,
@@ -199,8 +200,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     unsigned* __restrict__ counters, int H_q, int H_kv, int G, int S_max, int ntok, int chunk,
     int num_splits, float scale_log2) {
   using P = Dec<T, D>;
-  __shared__ __attribute__((aligned(16))) float lds_state[kWaves][4][4];  // m, l, bs, cref per head
-  __shared__ float lds_vec[kWaves][2][4][D];         // A, C per head
+  constexpr int HW = 4 * HG;                         // query heads per workgroup
+  __shared__ __attribute__((aligned(16))) float lds_state[kWaves][HW][4];  // m, l, bs, cref per head
+  __shared__ float lds_vec[kWaves][2][HW][D];        // A, C per head
   __shared__ __attribute__((aligned(16))) char k_lds[kWaves][P::KLDS];  // bf16: each wave's K block
 
   // Grid (KV head x head group, sequence, split): workgroups are dealt to
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   // power-of-two split count put split s of every stream on one XCD, and the
   // mostly empty high splits of a ragged batch left some XCDs with far more
   // work than others.
-  const int ngroups = (G + 3) / 4;
+  const int ngroups = (G + HW - 1) / HW;
   int hk = blockIdx.x / ngroups;
   int hgrp = blockIdx.x % ngroups;
   int b = blockIdx.y;
@@ -231,8 +233,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       split = (int)(rest / ((unsigned)H_kv * gridDim.y));
     }
   }
-  const int Gw = min(4, G - 4 * hgrp);               // heads in this workgroup
-  const int h0 = hk * G + 4 * hgrp;                  // first query head
+  const int Gw = min(HW, G - HW * hgrp);             // heads in this workgroup
+  const int h0 = hk * G + HW * hgrp;                 // first query head
 
   int n, past = 0, clen = 0;
   if constexpr (MT) {
@@ -261,18 +263,26 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int c = lane & 15;                           // lane column (0..15)
   const int hq = c >> 2;                             // head whose scores this lane holds
   const int t = c & 3;                               // 0,1: q / e rows; 2,3: rho / e*r rows
-  // keys this lane's head sees: all n, or, per token, the causal prefix
-  int lim = n;
-  if constexpr (MT) {
-    const int tok = (h0 + hq) % ntok;
-    lim = tok < clen ? past + tok + 1 : 0;
+  // Heads 4 hg + hq (hg < HG) of the workgroup: with HG = 2 a second probe
+  // tile (and a second set of value accumulators) serves four more heads
+  // from the same K and V reads.
+  // Keys each of this lane's heads sees: all n, or, per token, the causal prefix.
+  int lim[HG];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    lim[hg] = n;
+    if constexpr (MT) {
+      const int tok = (h0 + 4 * hg + hq) % ntok;
+      lim[hg] = tok < clen ? past + tok + 1 : 0;
+    }
   }
 
   // Probe operand (B of the score MFMA): column c, dims 32 kk + 8 g + (0..7).
-  bf16x8 pr_hi[P::KSTEPS], pr_lo[P::KSTEPS];
-  {
-    const bool live = hq < Gw;
-    const T* src = (t < 2 ? q : rho) + ((size_t)b * H_q + h0 + (live ? hq : 0)) * D;
+  bf16x8 pr_hi[HG][P::KSTEPS], pr_lo[HG][P::KSTEPS];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    const bool live = 4 * hg + hq < Gw;
+    const T* src = (t < 2 ? q : rho) + ((size_t)b * H_q + h0 + (live ? 4 * hg + hq : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < P::KSTEPS; ++kk) {
       uint32_t w[P::KW];
@@ -281,7 +291,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
         for (int i = 0; i < P::KW; ++i) w[i] = 0;
       }
-      to_operand<T>(w, pr_hi[kk], pr_lo[kk]);
+      to_operand<T>(w, pr_hi[hg][kk], pr_lo[hg][kk]);
     }
   }
 
@@ -289,12 +299,18 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + slice, (uint32_t)n * P::ROWB);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + slice, (uint32_t)n * P::ROWB);
 
-  f32x4 acc[P::DPL];
+  f32x4 acc[HG][P::DPL];
 #pragma unroll
-  for (int j = 0; j < P::DPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max (log2 units) for head hq
-  float lsum = 0.f;     // this lane's partial of l (t == 0) or Bs (t == 2)
-  float cref = 0.f;     // probe reference for head hq
+  for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+    for (int j = 0; j < P::DPL; ++j) acc[hg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[HG], lsum[HG], cref[HG];  // per head 4 hg + hq: running max (log2 units),
+#pragma unroll                       // this lane's part of l (t == 0) or Bs (t == 2),
+  for (int hg = 0; hg < HG; ++hg) {  // and the probe reference
+    m[hg] = -INFINITY;
+    lsum[hg] = 0.f;
+    cref[hg] = 0.f;
+  }
   bool first = true;
 
   // K pieces for the score MFMA and V rows for the value MFMA of one block.
@@ -350,10 +366,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
 
     // ---- scores: lane (g, c) gets probe column c for keys 16 T2 + 4 g + i
-    f32x4 sc[2];
+    f32x4 sc[HG][2];
 #pragma unroll
     for (int T2 = 0; T2 < 2; ++T2) {
-      sc[T2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) sc[hg][T2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < P::KSTEPS; ++kk) {
         bf16x8 khi, klo;
@@ -361,64 +378,72 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
           khi = kop[T2][kk];
         else
           to_operand<T>(kw[T2][kk].w, khi, klo);
-        sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_hi[kk], sc[T2], 0, 0, 0);
-        if constexpr (P::F32) {
-          sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_lo[kk], sc[T2], 0, 0, 0);
-          sc[T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, pr_hi[kk], sc[T2], 0, 0, 0);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          sc[hg][T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_hi[hg][kk], sc[hg][T2], 0, 0, 0);
+          if constexpr (P::F32) {
+            sc[hg][T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, pr_lo[hg][kk], sc[hg][T2], 0, 0, 0);
+            sc[hg][T2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, pr_hi[hg][kk], sc[hg][T2], 0, 0, 0);
+          }
         }
       }
     }
 
-    float x[8], rv[8];
-    float mx = -INFINITY;
+    const bool take_ref = first;
+    first = false;
+    bf16x8 aop[HG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float raw = sc[e >> 2][e & 3];
-      const int key = blk + 16 * (e >> 2) + 4 * g + (e & 3);
-      float s = quad_perm_0101(raw) * scale_log2;
-      s = key < j1 && (!MT || key < lim) ? s : -INFINITY;
-      x[e] = s;
-      rv[e] = raw;
-      mx = fmaxf(mx, s);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-    if (first) {
-      // reference: r of the first key of this wave's first block (lane 4h+2, slot 0)
-      cref = __shfl(rv[0], 4 * hq + 2);
-      first = false;
-    }
-
-    const bool need = mx > m + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float mnew = need ? mx : m;
-      const float alpha = need ? exp2f(m - mnew) : 1.0f;
-      m = mnew;
-      lsum *= alpha;
-      const float a_acc = __shfl(alpha, 4 * g);  // accumulator rows belong to head g
-#pragma unroll
-      for (int j = 0; j < P::DPL; ++j) acc[j] *= a_acc;
-    }
-
-    // ---- value-MFMA A operand: row c = 4h + t, key slots (g, e)
-    uint32_t aw[4];
-    {
-      float a[8];
+    for (int hg = 0; hg < HG; ++hg) {
+      float x[8], rv[8];
+      float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // With MT a head may have no visible key yet (m still -inf).
-        const float p = (MT && x[e] == -INFINITY) ? 0.f : exp2f(x[e] - m);
-        float val = t >= 2 ? p * (rv[e] - cref) : p;
-        val = hq < Gw ? val : 0.f;
-        lsum += val;
-        const float hi = bf16_round(val);
-        a[e] = (t & 1) ? val - hi : val;
+        const float raw = sc[hg][e >> 2][e & 3];
+        const int key = blk + 16 * (e >> 2) + 4 * g + (e & 3);
+        float s = quad_perm_0101(raw) * scale_log2;
+        s = key < j1 && (!MT || key < lim[hg]) ? s : -INFINITY;
+        x[e] = s;
+        rv[e] = raw;
+        mx = fmaxf(mx, s);
       }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+      if (take_ref) {
+        // reference: r of the first key of this wave's first block (lane 4h+2, slot 0)
+        cref[hg] = __shfl(rv[0], 4 * hq + 2);
+      }
+
+      const bool need = mx > m[hg] + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mnew = need ? mx : m[hg];
+        const float alpha = need ? exp2f(m[hg] - mnew) : 1.0f;
+        m[hg] = mnew;
+        lsum[hg] *= alpha;
+        const float a_acc = __shfl(alpha, 4 * g);  // accumulator rows belong to head g
 #pragma unroll
-      for (int u = 0; u < 4; ++u) aw[u] = pack_bf16(a[2 * u], a[2 * u + 1]);
+        for (int j = 0; j < P::DPL; ++j) acc[hg][j] *= a_acc;
+      }
+
+      // ---- value-MFMA A operand: row c = 4h + t, key slots (g, e)
+      uint32_t aw[4];
+      {
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // With MT a head may have no visible key yet (m still -inf).
+          const float p = (MT && x[e] == -INFINITY) ? 0.f : exp2f(x[e] - m[hg]);
+          float val = t >= 2 ? p * (rv[e] - cref[hg]) : p;
+          val = 4 * hg + hq < Gw ? val : 0.f;
+          lsum[hg] += val;
+          const float hi = bf16_round(val);
+          a[e] = (t & 1) ? val - hi : val;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) aw[u] = pack_bf16(a[2 * u], a[2 * u + 1]);
+      }
+      aop[hg] = as_bf16x8(aw[0], aw[1], aw[2], aw[3]);
     }
-    const bf16x8 aop = as_bf16x8(aw[0], aw[1], aw[2], aw[3]);
 
     // ---- values: N-tile j covers dims (d/16) c + j
 #pragma unroll
@@ -428,8 +453,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           bw[u] = pair_halves(vw[2 * u].w[j >> 1], vw[2 * u + 1].w[j >> 1], j & 1);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, as_bf16x8(bw[0], bw[1], bw[2], bw[3]),
-                                                         acc[j], 0, 0, 0);
+        const bf16x8 bop = as_bf16x8(bw[0], bw[1], bw[2], bw[3]);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg)
+          acc[hg][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[hg], bop, acc[hg][j], 0, 0, 0);
       } else {
         float vv[8], vr[8];
 #pragma unroll
@@ -441,28 +468,34 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
                                      pack_bf16(vv[4], vv[5]), pack_bf16(vv[6], vv[7]));
         const bf16x8 blo = as_bf16x8(pack_bf16(vr[0], vr[1]), pack_bf16(vr[2], vr[3]),
                                      pack_bf16(vr[4], vr[5]), pack_bf16(vr[6], vr[7]));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bhi, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, blo, acc[j], 0, 0, 0);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          acc[hg][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[hg], bhi, acc[hg][j], 0, 0, 0);
+          acc[hg][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[hg], blo, acc[hg][j], 0, 0, 0);
+        }
       }
     }
   }
 
-  // ---- per-wave state to LDS
-  float tot = lsum + __shfl_xor(lsum, 16);
-  tot += __shfl_xor(tot, 32);
-  if (g == 0 && hq < 4) {
-    if (t == 0) {
-      lds_state[wave][hq][0] = m;
-      lds_state[wave][hq][1] = first ? 0.f : tot;
-      lds_state[wave][hq][3] = cref;
-    } else if (t == 2) {
-      lds_state[wave][hq][2] = first ? 0.f : tot;
-    }
-  }
+  // ---- per-wave state to LDS (a wave without blocks leaves l = 0)
 #pragma unroll
-  for (int j = 0; j < P::DPL; ++j) {
-    lds_vec[wave][0][g][P::DPL * c + j] = acc[j][0] + acc[j][1];
-    lds_vec[wave][1][g][P::DPL * c + j] = acc[j][2] + acc[j][3];
+  for (int hg = 0; hg < HG; ++hg) {
+    float tot = lsum[hg] + __shfl_xor(lsum[hg], 16);
+    tot += __shfl_xor(tot, 32);
+    if (g == 0) {
+      if (t == 0) {
+        lds_state[wave][4 * hg + hq][0] = m[hg];
+        lds_state[wave][4 * hg + hq][1] = first ? 0.f : tot;
+        lds_state[wave][4 * hg + hq][3] = cref[hg];
+      } else if (t == 2) {
+        lds_state[wave][4 * hg + hq][2] = first ? 0.f : tot;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < P::DPL; ++j) {
+      lds_vec[wave][0][4 * hg + g][P::DPL * c + j] = acc[hg][j][0] + acc[hg][j][1];
+      lds_vec[wave][1][4 * hg + g][P::DPL * c + j] = acc[hg][j][2] + acc[hg][j][3];
+    }
   }
   __syncthreads();
 
@@ -569,17 +602,23 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const int32_t* __res
       merge_records<D>(ws + (size_t)bh * num_splits * REC, nsv, threadIdx.x);
 }
 
-template <typename T, int D, bool MT>
-hipError_t launch_partial_t(const DecodeArgs& a, hipStream_t st) {
-  const int ngroups = (a.G + 3) / 4;
+template <typename T, int D, bool MT, int HG>
+hipError_t launch_partial_hg(const DecodeArgs& a, hipStream_t st) {
+  const int ngroups = (a.G + 4 * HG - 1) / (4 * HG);
   dim3 grid(a.H_kv * ngroups, a.B, a.num_splits);  // stream fastest in the linear order
-  hipLaunchKernelGGL((decode_partial_kernel<T, D, MT>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((decode_partial_kernel<T, D, MT, HG>), grid, dim3(256), 0, st,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.rho),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.seq_lens,
                      a.past_lens, a.out, static_cast<float*>(a.ws),
                      static_cast<unsigned*>(a.counters), a.H_q, a.H_kv, a.G, a.S_max, a.ntok,
                      a.chunk, a.num_splits, a.scale * kLog2e);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool MT>
+hipError_t launch_partial_t(const DecodeArgs& a, hipStream_t st) {
+  return decode_heads_per_workgroup(a.G) == 8 ? launch_partial_hg<T, D, MT, 2>(a, st)
+                                              : launch_partial_hg<T, D, MT, 1>(a, st);
 }
 
 template <bool MT>

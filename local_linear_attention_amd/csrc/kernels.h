@@ -73,6 +73,11 @@ struct ProjArgs {
   int B, T, d_model, H_q, H_kv, d, S_max;
 };
 
+// Query heads one decode workgroup serves: 8 (two probe tiles) when a KV
+// head has more than 4, else 4. The split plan counts workgroup streams of
+// this many heads.
+inline int decode_heads_per_workgroup(int G) { return G > 4 ? 8 : 4; }
+
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
