@@ -168,7 +168,9 @@ class DecodeRunner:
         return (t1 - t0) / steps, ev0.elapsed_time(ev1) / steps / 1e3
 
 
-def bench_prefill(w, steps, warmup, seed=None):
+def bench_prefill(w, steps, warmup, seed=None, keep=None):
+    """Causal prefill per step. With `keep` (a dict), the inputs and the last
+    output stay there for the oracle's timing leg."""
     import torch
 
     import local_linear_attention_amd as pa
@@ -196,6 +198,8 @@ def bench_prefill(w, steps, warmup, seed=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = ev0.elapsed_time(ev1) / steps / 1e3
+    if keep is not None:
+        keep.update(inp=inp, out=out)
     # algorithmic work: q.k, rho.k, e.v and (e r).v over the causal half, 2 d flops each
     flops = 8.0 * w.d * (w.T * (w.T + 1) / 2) * w.B * w.H_q
     return {"us_per_step": (t1 - t0) / steps * 1e6, "kernel_us": kern * 1e6,
@@ -372,11 +376,75 @@ def bench_tokens(T, steps, warmup, seed=None):
             "shape": dict(B=w.B, H_q=w.H_q, H_kv=w.H_kv, d=w.d, new_tokens=T, cached=w.past)}
 
 
-def cpu_baseline(runner, min_s=10.0, budget_s=30.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def prefill_oracle_sample(w, keep, min_s=5.0, n_rows=16):
+    """Times the fp64 prefill oracle on the causal-prefill workload.
+
+    Two legs: every row of (b, h) pairs, taken in order until at least `min_s`
+    seconds have accumulated, through the dense masked-matrix form; and
+    `n_rows` single rows spread over the positions through the explicit
+    d x d Sigma_KV form. Both are compared with the GPU output of the same
+    inputs.
+    """
+    import numpy as np
+
+    import oracle
+
+    inp, got = keep["inp"], keep["out"]
+    G = w.H_q // w.H_kv
+    t_full = 0.0
+    err = 0.0
+    pairs = []
+    for b in range(w.B):
+        for h in range(w.H_q):
+            if t_full >= min_s:
+                break
+            args = [inp["q"][b:b + 1, h:h + 1], inp["rho"][b:b + 1, h:h + 1],
+                    inp["k"][b:b + 1, h // G:h // G + 1], inp["v"][b:b + 1, h // G:h // G + 1],
+                    inp["seq_lens"][b:b + 1]]
+            args = [a.cpu() for a in args]
+            t0 = time.perf_counter()
+            full = oracle.oracle_prefill_full(*args, inp["scale"])[(0, 0)]
+            t_full += time.perf_counter() - t0
+            g = got[b, h].cpu().numpy()
+            err = max(err, float(np.max(np.abs(g - full).max(axis=1) / np.abs(full).max(axis=1))))
+            pairs.append((b, h))
+    rows = [((i + 1) % w.B, (7 * i + 1) % w.H_q, (w.T - 1) * (i + 1) // n_rows)
+            for i in range(n_rows)]
+    t0 = time.perf_counter()
+    ref = oracle.oracle_prefill_rows(inp["q"].cpu(), inp["rho"].cpu(), inp["k"].cpu(),
+                                     inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"], rows)
+    t_rows = time.perf_counter() - t0
+    for (b, h, t), o in ref.items():
+        err = max(err, float(np.abs(got[b, h, t].cpu().numpy() - o).max() / np.abs(o).max()))
+    pair_flops = 8.0 * w.d * w.T * (w.T + 1) / 2
+    return {"seconds_per_pair": t_full / len(pairs),
+            "gflops": pair_flops * len(pairs) / t_full / 1e9,
+            "pairs_sample": f"all {w.T} rows of {len(pairs)} (b, h) pairs, dense masked T x T "
+                            f"fp64 NumPy, {t_full:.1f} s",
+            "rows_seconds": t_rows,
+            "rows_sample": f"{len(rows)} explicit rows (d x d Sigma_KV each) at positions "
+                           f"spread over 0..{w.T - 1}",
+            "gpu_vs_oracle_max_rel_err": err}
+
+
+def cpu_baseline(runner, min_s=10.0, budget_s=30.0, prefill=None):
     """Times the fp64 oracle on a bounded sample of the GQA decode workload.
 
     Query heads are taken in order, cycling over the workload, until at least
     `min_s` seconds of oracle time (or `budget_s` at most) have accumulated.
+    With `prefill` = (workload, kept inputs and output), the prefill oracle is
+    timed as well (``prefill_oracle_sample``).
     """
     import numpy as np
 
@@ -414,14 +482,18 @@ def cpu_baseline(runner, min_s=10.0, budget_s=30.0):
             break
     frac = done / len(pairs)
     gbs = runner.kv_bytes * frac / t_total / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} query-head evaluations ({frac:.2f} passes over the {len(pairs)} "
-                      f"query heads of the gqa-decode workload; fp64 NumPy, explicit d x d "
-                      f"Sigma_KV), {t_total:.1f} s of oracle time; GB/s is the workload's KV "
-                      f"stream times the passes completed, over that time",
-            "seconds": t_total, "gpu_vs_oracle_max_rel_err": err,
-            "host_cpus": os.cpu_count(),
-            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+    res = {"value": gbs, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} query-head evaluations ({frac:.2f} passes over the {len(pairs)} "
+                     f"query heads of the gqa-decode workload; fp64 NumPy, explicit d x d "
+                     f"Sigma_KV), {t_total:.1f} s of oracle time; GB/s is the workload's KV "
+                     f"stream times the passes completed, over that time",
+           "seconds": t_total, "gpu_vs_oracle_max_rel_err": err,
+           "host_cpus": os.cpu_count(),
+           "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+           "blas_threads": int(threads), "cpu_model": cpu_model()}
+    if prefill is not None:
+        res["causal_prefill"] = prefill_oracle_sample(*prefill)
+    return res
 
 
 def main():
@@ -521,6 +593,7 @@ def main():
         log(f"plain read of the same bytes: {read_gbs:.0f} GB/s")
 
     workloads = {}
+    prefill_keep = None if args.no_cpu_baseline else {}
     if args.workloads == "all":
         for idx, nbuf in ((1, 1), (3, 1), (4, 2)):
             wi = WORKLOADS[idx]
@@ -551,7 +624,8 @@ def main():
             workloads[f"multi-token-decode-T{T}"] = bench_tokens(T, args.steps, max(3, args.warmup // 4))
             torch.cuda.empty_cache()
         log("workload causal-prefill")
-        workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10)
+        workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10,
+                                                     keep=prefill_keep)
         log("workload chunked-prefill")
         workloads[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
         log("workload causal-prefill-backward")
@@ -562,7 +636,8 @@ def main():
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(main_r)
+        result["cpu_baseline"] = cpu_baseline(
+            main_r, prefill=(WORKLOADS[5], prefill_keep) if prefill_keep else None)
     print(json.dumps(result), flush=True)
 
 
