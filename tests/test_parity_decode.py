@@ -121,9 +121,11 @@ def test_random_shapes(case):
 
 
 def test_head_groups_placed_together():
-    """G = 8 and 12 take two and three head groups per KV head, whose workgroups
-    are placed on one XCD (grid sizes divisible by 8 x groups)."""
-    for G in (8, 12):
+    """More than 4 query heads per KV head: one 8-head workgroup (two probe
+    tiles) per KV head and split at G = 8, and several head groups at G = 12
+    (8 + 4 heads) and G = 16 (8 + 8), whose workgroups are placed on one XCD
+    when the grid size is divisible by 8 x groups."""
+    for G in (8, 12, 16):
         w = replace_shape(WORKLOADS[2], B=4, H_q=G * 4, H_kv=4, S_max=1024)
         check(w, seq_lens=[1024, 1000, 517, 3], num_splits=(0, 2, 4))
 
@@ -226,6 +228,14 @@ def _sampled(w, heads, seed=None, gen_device="cuda"):
     print(f"   max rel err {max(errs):.3e}", flush=True)
     assert max(errs) < TOL
     assert np.isfinite(got).all()
+
+
+def test_gqa8_full_size_sampled():
+    """The G = 8 decode (64 query heads on 8 KV heads, 8 x 4096 keys) in the
+    automatic plan that the benchmark times: every head of two KV heads."""
+    w = replace_shape(WORKLOADS[2], name="gqa8-decode", H_q=64)
+    heads = [(0, h) for h in range(8)] + [(7, h) for h in range(56, 64)]
+    _sampled(w, heads)
 
 
 @pytest.mark.slow
