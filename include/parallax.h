@@ -45,10 +45,10 @@
  *    stream). Every argument check happens on the host before any launch: on
  *    an error status nothing has been launched and no buffer was touched.
  *    Launch failures return PARALLAX_ERR_HIP. No call throws.
- *  - Supported: head dim d in {64, 128}; G = H_q / H_kv integral with
- *    G <= 4 or G a multiple of 4 (groups of 4 query heads share one pass over
- *    their KV head; larger G re-reads K/V once per group of 4); each (b, h_kv)
- *    slice of K or V must be smaller than 2 GiB.
+ *  - Supported: head dim d in {64, 128}; any integral G = H_q / H_kv (up
+ *    to 4 query heads, or up to 8 when G > 4, share one pass over their KV
+ *    head; G > 8 re-reads K and V once per further group of 8); each
+ *    (b, h_kv) slice of K or V must be smaller than 2 GiB.
  */
 #ifndef PARALLAX_H
 #define PARALLAX_H
@@ -211,8 +211,8 @@ parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const
  *               H_kv, S_max, num_splits) and the size
  *               parallax_decode_workspace_size(B, H_q * T, d, num_splits);
  *               the same zeroed-counter rule applies.
- * Limits: (H_q / H_kv) * T must be at most 4 or a multiple of 4
- * (PARALLAX_ERR_UNSUPPORTED otherwise). Other errors as parallax_decode, plus
+ * Errors as parallax_decode (any number (H_q / H_kv) * T of (head, token)
+ * pairs per KV head is supported), plus
  * PARALLAX_ERR_NULL_POINTER for a NULL past_lens or chunk_lens and
  * PARALLAX_ERR_BAD_SHAPE for T <= 0 or T > S_max.
  */

@@ -115,7 +115,6 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   if (dtype != PARALLAX_BF16 && dtype != PARALLAX_F32) return PARALLAX_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
   const int G = H_q / H_kv;
-  if (G > 4 && G % 4 != 0) return PARALLAX_ERR_UNSUPPORTED;
   const long long esz = dtype == PARALLAX_F32 ? 4 : 2;
   if (((long long)S_max + 64) * d * esz >= (1LL << 31)) return PARALLAX_ERR_UNSUPPORTED;
   if (B > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y

@@ -102,7 +102,6 @@ def test_decode_argument_errors(L, fn):
     assert _decode(L, fn, scale=float("inf")) == SHAPE
     assert _decode(L, fn, d=96) == UNSUP
     assert _decode(L, fn, dtype=7) == UNSUP
-    assert _decode(L, fn, Hq=6, Hkv=1) == UNSUP  # G = 6: not <= 4 and not a multiple of 4
     assert _decode(L, fn, S=1 << 24) == UNSUP    # a (b, h_kv) slice of 4 GiB
     assert _decode(L, fn, S=(1 << 23) - 64) == UNSUP  # (S + 64) d 2 bytes reaches 2^31
     assert _decode(L, fn, k=P + 8) == MISAL
@@ -172,7 +171,6 @@ def test_decode_tokens_argument_errors(L):
     assert _tokens(L, T=0) == SHAPE
     assert _tokens(L, T=513) == SHAPE             # more tokens than cache rows
     assert _tokens(L, Hq=3, Hkv=2) == SHAPE       # H_q not a multiple of H_kv
-    assert _tokens(L, Hq=2, Hkv=1, T=3) == UNSUP  # 6 (head, token) pairs per KV head
     assert _tokens(L, d=96) == UNSUP
     assert _tokens(L, past=P + 2) == MISAL
     assert _tokens(L, ws_bytes=16) == WS

@@ -80,7 +80,8 @@ def test_edge_lengths(n):
     check(w, seq_lens=[n, 512 - n], num_splits=(1, 2, 4))
 
 
-@pytest.mark.parametrize("G,H_kv", [(1, 3), (2, 2), (3, 2), (4, 2), (8, 1), (12, 1)])
+@pytest.mark.parametrize("G,H_kv", [(1, 3), (2, 2), (3, 2), (4, 2), (5, 2), (6, 1), (7, 2),
+                                    (8, 1), (10, 1), (12, 1), (13, 1)])
 def test_group_sizes(G, H_kv):
     w = replace_shape(WORKLOADS[2], B=2, H_q=G * H_kv, H_kv=H_kv, S_max=300)
     check(w, seq_lens=[300, 161], num_splits=(0, 1))
@@ -98,7 +99,7 @@ def _random_cases(count, seed):
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(count):
-        G = int(rng.choice([1, 2, 3, 4, 8, 12]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 10, 12]))
         H_kv = int(rng.integers(1, 4))
         d = int(rng.choice([64, 128]))
         dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
@@ -125,7 +126,7 @@ def test_head_groups_placed_together():
     tiles) per KV head and split at G = 8, and several head groups at G = 12
     (8 + 4 heads) and G = 16 (8 + 8), whose workgroups are placed on one XCD
     when the grid size is divisible by 8 x groups."""
-    for G in (8, 12, 16):
+    for G in (6, 8, 12, 16):
         w = replace_shape(WORKLOADS[2], B=4, H_q=G * 4, H_kv=4, S_max=1024)
         check(w, seq_lens=[1024, 1000, 517, 3], num_splits=(0, 2, 4))
 

@@ -66,11 +66,12 @@ def small(**kw):
 @pytest.mark.parametrize("T", [1, 2, 4])
 def test_group_of_two(T):
     """G = 2 (the gqa shape's group): T = 1, 2 fit one group of 4 (head, token)
-    pairs; T = 4 takes two."""
+    pairs; T = 4 fills one 8-pair workgroup (two probe tiles)."""
     check(small(T=T), past_lens=[700, 33, 256], chunk_lens=[T, max(T - 1, 0), T], S_max=720)
 
 
-@pytest.mark.parametrize("G,H_kv,T", [(1, 3, 4), (4, 1, 1), (4, 2, 2), (8, 1, 2), (2, 2, 8)])
+@pytest.mark.parametrize("G,H_kv,T", [(1, 3, 4), (4, 1, 1), (4, 2, 2), (8, 1, 2), (2, 2, 8),
+                                      (2, 2, 3), (1, 2, 5), (2, 1, 5), (3, 2, 3)])
 def test_group_sizes_and_tokens(G, H_kv, T):
     check(small(H_q=G * H_kv, H_kv=H_kv, T=T), past_lens=[400, 0, 129],
           chunk_lens=[T, T, 1], S_max=420)
