@@ -16,7 +16,7 @@ average launch duration for the `roofline` object. The other workloads (single-h
 128K-context split-KV decode, causal prefill) are timed the same way, briefly,
 and reported under "workloads", with a chunked prefill (1024 new rows after
 3072 cached tokens), the GQA decode shape at 64 query heads on 8 KV heads, and
-multi-token decode (2 and 4 new tokens per sequence at the GQA decode shape). The `cpu_baseline` leg times the fp64 oracle
+multi-token decode (2, 3 and 4 new tokens per sequence at the GQA decode shape). The `cpu_baseline` leg times the fp64 oracle
 on a bounded sample of the same GQA decode workload on the host cores.
 
 One JSON line is printed at the end.
@@ -619,7 +619,7 @@ def main():
             "num_splits": r.ns, "chunk": r.chunk, "shape": dict(B=8, H_q=64, H_kv=8, d=128, kv_len=4096)}
         del r
         torch.cuda.empty_cache()
-        for T in (2, 4):
+        for T in (2, 3, 4):
             log(f"workload multi-token-decode T={T}")
             workloads[f"multi-token-decode-T{T}"] = bench_tokens(T, args.steps, max(3, args.warmup // 4))
             torch.cuda.empty_cache()
