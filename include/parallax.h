@@ -81,7 +81,8 @@ int parallax_abi_version(void);
 const char* parallax_status_string(parallax_status_t s);
 
 /*
- * Split-KV plan for decode. Each (b, KV head, group of <= 4 query heads) is
+ * Split-KV plan for decode. Each (b, KV head, group of <= 4 query heads, or
+ * <= 8 when the KV head serves more than 4) is
  * cut into `num_splits` contiguous key ranges of `chunk` keys (a multiple of
  * 128), processed by separate workgroups whose partial softmax states are
  * merged by the combine step. `requested` = 0 picks a plan from the device's
