@@ -149,3 +149,32 @@ def test_gqa_shape_four_tokens_sampled():
     err = max(rel_err(got[b, h, t][None], o[None]) for (b, h, t), o in ex.items())
     print(f"   sampled rows: {err:.3e}", flush=True)
     assert err < TOL
+
+
+def _random_cases(n=10, seed=20261203):
+    """Seeded shapes that combine group size, token count, head dim, dtype,
+    cache size, past and chunk lengths (past may run past the cache, which
+    clamps the chunk) and split count."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        G = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        H_kv = int(rng.integers(1, 4))
+        T = int(rng.integers(1, 9))
+        d = int(rng.choice([64, 128]))
+        dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+        B = int(rng.integers(1, 4))
+        S = int(rng.integers(T, 900))
+        past = [int(x) for x in rng.integers(0, S + 1, B)]
+        clen = [int(x) for x in rng.integers(0, T + 1, B)]
+        cases.append((G, H_kv, T, d, dtype, B, S, past, clen, int(rng.integers(2, 8))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(),
+                         ids=lambda c: f"G{c[0]}-Hkv{c[1]}-T{c[2]}-d{c[3]}-S{c[6]}")
+def test_random_shapes(case):
+    G, H_kv, T, d, dtype, B, S, past, clen, ns = case
+    w = small(B=B, T=T, H_q=G * H_kv, H_kv=H_kv, d=d, dtype=dtype, q_std=d ** -0.25,
+              k_std=d ** -0.25)
+    check(w, past_lens=past, chunk_lens=clen, S_max=S, num_splits=(0, 1, ns))
