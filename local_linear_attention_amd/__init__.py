@@ -148,6 +148,28 @@ def _dev_tensor(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _one_device(*named):
+    """Every (name, tensor) pair on the first one's device (a kernel reads all
+    of them on that device)."""
+    dev = named[0][1].device
+    for name, t in named[1:]:
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, not on {dev} with {named[0][0]}")
+
+
+def _out_tensor(out, shape, device):
+    """A fresh fp32 output, or the caller's after checking that the kernels
+    can write all of it in place."""
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _dev_tensor(out, "out")
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must be float32 of shape {tuple(shape)}")
+    if out.device != device:
+        raise ValueError(f"out is on {out.device}, the inputs on {device}")
+    return out
+
+
 def _stream_ptr(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -179,6 +201,8 @@ def _decode_shapes(q, rho, k_cache, v_cache, seq_lens):
         raise TypeError("q, rho, k_cache and v_cache must share one dtype")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
+    _one_device(("q", q), ("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache),
+                ("seq_lens", seq_lens))
     return B, H_q, H_kv, d, S_max
 
 
@@ -188,6 +212,10 @@ def _workspace(B, H_q, H_kv, d, S_max, num_splits, workspace, device):
     if workspace is None:
         # zeroed: the fused merge's arrival counters must start at zero
         workspace = torch.zeros(max(need, 16) // 4, dtype=torch.float32, device=device)
+    else:
+        _dev_tensor(workspace, "workspace")
+        if workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, the inputs on {device}")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -195,8 +223,7 @@ def decode(q, rho, k_cache, v_cache, seq_lens, scale: float, *, num_splits: int 
            workspace=None):
     """Parallax decode; returns out [B, H_q, d] fp32 (see parallax_decode)."""
     B, H_q, H_kv, d, S_max = _decode_shapes(q, rho, k_cache, v_cache, seq_lens)
-    if out is None:
-        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    out = _out_tensor(out, (B, H_q, d), q.device)
     ws, ws_bytes = _workspace(B, H_q, H_kv, d, S_max, num_splits, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(lib().parallax_decode(
@@ -211,6 +238,10 @@ def decode_partial(q, rho, k_cache, v_cache, seq_lens, scale: float, workspace, 
                    num_splits: int = 0, out=None):
     """First decode phase (partial states into ``workspace``; see parallax_decode_partial)."""
     B, H_q, H_kv, d, S_max = _decode_shapes(q, rho, k_cache, v_cache, seq_lens)
+    if out is not None:
+        out = _out_tensor(out, (B, H_q, d), q.device)
+    _dev_tensor(workspace, "workspace")
+    _one_device(("q", q), ("workspace", workspace))
     ws_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         _check(lib().parallax_decode_partial(
@@ -223,8 +254,14 @@ def decode_partial(q, rho, k_cache, v_cache, seq_lens, scale: float, workspace, 
 
 def decode_combine(seq_lens, out, workspace, *, H_kv: int, S_max: int, num_splits: int = 0):
     """Second decode phase: merges the workspace into ``out`` [B, H_q, d]."""
-    _dev_tensor(out, "out")
+    for name, t in (("seq_lens", seq_lens), ("out", out), ("workspace", workspace)):
+        _dev_tensor(t, name)
+    if out.dim() != 3 or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [B, H_q, d]")
     B, H_q, d = out.shape
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    _one_device(("out", out), ("seq_lens", seq_lens), ("workspace", workspace))
     ws_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(out.device):
         _check(lib().parallax_decode_combine(
@@ -247,8 +284,8 @@ def prefill(q, rho, k, v, seq_lens, scale: float, *, out=None):
         raise TypeError("q, rho, k and v must share one dtype")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
-    if out is None:
-        out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    _one_device(("q", q), ("rho", rho), ("k", k), ("v", v), ("seq_lens", seq_lens))
+    out = _out_tensor(out, (B, H_q, T, d), q.device)
     with torch.cuda.device(q.device):
         _check(lib().parallax_prefill(
             q.data_ptr(), rho.data_ptr(), k.data_ptr(), v.data_ptr(), seq_lens.data_ptr(),
@@ -273,6 +310,8 @@ def _chunk_shapes(q, rho, k_cache, v_cache, past_lens, chunk_lens):
     for name, t in (("past_lens", past_lens), ("chunk_lens", chunk_lens)):
         if t.dtype != torch.int32 or t.shape != (B,):
             raise ValueError(f"{name} must be int32 [B]")
+    _one_device(("q", q), ("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache),
+                ("past_lens", past_lens), ("chunk_lens", chunk_lens))
     return B, H_q, T, H_kv, d, S_max
 
 
@@ -283,8 +322,7 @@ def prefill_chunked(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: floa
     parallax_prefill_chunked). Returns out [B, H_q, T, d] fp32.
     """
     B, H_q, T, H_kv, d, S_max = _chunk_shapes(q, rho, k_cache, v_cache, past_lens, chunk_lens)
-    if out is None:
-        out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    out = _out_tensor(out, (B, H_q, T, d), q.device)
     with torch.cuda.device(q.device):
         _check(lib().parallax_prefill_chunked(
             q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -299,8 +337,7 @@ def decode_tokens(q, rho, k_cache, v_cache, past_lens, chunk_lens, scale: float,
     sequence, by the split-KV decode kernel (see parallax_decode_tokens).
     Returns out [B, H_q, T, d] fp32."""
     B, H_q, T, H_kv, d, S_max = _chunk_shapes(q, rho, k_cache, v_cache, past_lens, chunk_lens)
-    if out is None:
-        out = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
+    out = _out_tensor(out, (B, H_q, T, d), q.device)
     ws, ws_bytes = _workspace(B, H_q * T, H_kv, d, S_max, num_splits, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(lib().parallax_decode_tokens(
@@ -324,6 +361,7 @@ def _prefill_shapes(q, rho, k, v, seq_lens):
         raise TypeError("q, rho, k and v must share one dtype")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
+    _one_device(("q", q), ("rho", rho), ("k", k), ("v", v), ("seq_lens", seq_lens))
     return B, H_q, H_kv, T, S_max, d
 
 
@@ -367,6 +405,9 @@ def prefill_backward(q, rho, k, v, seq_lens, out, mu_v, stats, dout, scale: floa
     need = prefill_backward_workspace_size(B, H_q, T, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev_tensor(workspace, "workspace")
+    _one_device(("q", q), ("out", out), ("mu_v", mu_v), ("stats", stats), ("dout", dout),
+                ("workspace", workspace))
     ws_bytes = workspace.numel() * workspace.element_size()
     dq = torch.empty((B, H_q, T, d), dtype=torch.float32, device=q.device)
     drho = torch.empty_like(dq)
@@ -412,6 +453,8 @@ def qkvr_projection(x, w, H_q: int, H_kv: int, d: int, *, k_cache=None, v_cache=
         _dev_tensor(past_lens, "past_lens")
         if past_lens.dtype != torch.int32 or past_lens.shape != (B,):
             raise ValueError("past_lens must be int32 [B]")
+        _one_device(("x", x), ("past_lens", past_lens))
+    _one_device(("x", x), ("w", w), ("k_cache", k_cache), ("v_cache", v_cache))
     q = torch.empty((B, H_q, T, d), dtype=torch.bfloat16, device=x.device)
     rho = torch.empty_like(q)
     with torch.cuda.device(x.device):
@@ -433,6 +476,7 @@ def read_probe(a, b, sink):
     nbytes = a.numel() * a.element_size()
     if b.numel() * b.element_size() != nbytes or sink.dtype != torch.int32:
         raise ValueError("a and b must hold the same number of bytes; sink is int32")
+    _one_device(("a", a), ("b", b), ("sink", sink))
     with torch.cuda.device(a.device):
         _check(lib().parallax_read_probe(a.data_ptr(), b.data_ptr(), nbytes, sink.data_ptr(),
                                          sink.numel(), _stream_ptr(a.device)), "parallax_read_probe")
