@@ -13,12 +13,12 @@
 //
 // with, over keys j <= t, e_j = exp(s_tj - m), s_tj = scale q_t.k_j,
 // r_tj = rho_t.k_j - c_t, l = sum e, A = sum e v_j, Bs = sum e r, C = sum e r v_j.
-// The per-row reference c_t = rho_t.k_0 cancels exactly (it shifts Bs by
-// c l and C by c A) and keeps a large common offset of rho.k out of the
-// accumulated products.
+// Any per-row reference c_t cancels exactly (it shifts Bs by c l and C by
+// c A); it keeps a large common offset of rho.k out of the accumulated
+// products.
 //
 // Tiling. A workgroup of 8 waves owns 128 query rows of one (b, h); each wave
-// owns 16 rows, so a wave needs about 204 registers and two waves share each
+// owns 16 rows, so a wave needs about 195-202 registers and two waves share each
 // SIMD (while one waits on LDS or on a dependency the other issues; on gfx950
 // MFMA and VALU instructions of one SIMD never execute at the same time).
 // Key blocks of 32 keys are staged two at a time in double-buffered LDS (rows
@@ -29,15 +29,28 @@
 // (T = 0, 1; i = 0..3), which are exactly the 8 key slots that lane supplies
 // as the A operand of the value MFMA, so no data moves between lanes; row
 // statistics need two exchanges (lanes ^ 16, ^ 32). The value MFMA computes
-// [e; e r] V with e and e r each split into a bf16 high part and the bf16
-// rounding of the remainder (four products), so the fp32 weights reach the
-// bf16 contraction to about 2^-17. The V operand (key slots down, dims
-// across) comes straight from the row-major V tile through the CDNA4
-// transposing LDS load (ds_read_b64_tr_b16), so no lane shuffles V in
-// registers; output column c of N-tile j is dim 16 j + c. Softmax rescaling
-// is lazy (only when a block's max exceeds the running reference by more than
-// 2^8). Each workgroup handles a heavy (late) and a light (early) row block,
-// so every workgroup carries the same causal work.
+// [e; e r] V. The V operand (key slots down, dims across) comes straight
+// from the row-major V tile through the CDNA4 transposing LDS load
+// (ds_read_b64_tr_b16), so no lane shuffles V in registers; output column c
+// of N-tile j is dim 16 j + c. Softmax rescaling is lazy (only when a block's
+// max exceeds the running reference by more than 2^8). Each workgroup handles
+// a heavy (late) and a light (early) row block, so every workgroup carries
+// the same causal work.
+//
+// Weights of the value contraction. Inference (prefill, chunked prefill):
+// e and e (r - c) are rounded once to fp16 and V is staged as fp16 (exact for
+// bf16 values of magnitude 2^-14 .. 65504), two products per value tile.
+// l and Bs sum the same rounded weights, so A / l is an exact weighted mean
+// under weights perturbed by at most 2^-11 of themselves; the probe
+// reference c follows the running weighted mean of r (moved on the first
+// block and whenever a block's max jumps by more than 2^3), so the rounding
+// of e (r - c) stays small next to the weights that dominate a row. Measured
+// against the fp64 oracle: 3-6e-4 per row at the benchmark statistics, up to
+// about 1.3e-3 with probes 20x stronger and a sharp softmax. Training
+// forward (also writes mu_v and the row statistics the backward recomputes
+// the weights from): e and e (r - c) as a bf16 high part plus the bf16
+// rounding of the remainder (four products per value tile), about 2^-17,
+// with c = rho_t . k_0.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -46,12 +59,39 @@ namespace parallax {
 
 namespace {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f16x8 as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  i32x4 v = {(int)a, (int)b, (int)c, (int)d};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// Two fp32 -> packed fp16 pair, rounded toward zero (a in the low half). Out
+// of range values saturate to the largest finite fp16 instead of overflowing.
+__device__ __forceinline__ f16x2 pack_f16_rtz(float a, float b) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// 8 bf16 -> 8 fp16. Exact for magnitudes in [2^-14, 65504] (fp16 keeps all 8
+// significant bits of bf16 there); smaller ones lose bits below 2^-24.
+__device__ __forceinline__ i32x4 bf16x8_to_f16x8(i32x4 x) {
+  i32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = (uint32_t)x[i];
+    r[i] = __builtin_bit_cast(int, pack_f16_rtz(bf16_lo(w), bf16_hi(w)));
+  }
+  return r;
+}
+
 constexpr int kRows = 128;      // query rows per workgroup
 constexpr int kWaves = 8;       // 16 rows per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeys = 32;       // keys per block
 constexpr int kNB = 2;          // key blocks per barrier
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRefLog2 = 3.0f;       // block-max jump that moves the probe reference
 
 template <int D>
 struct Pre {
@@ -68,8 +108,11 @@ struct Pre {
   static constexpr int TILE = kKeys * VSTR;           // bytes of one staged K or V tile
 };
 
-// One row block (128 query rows starting at rb * 128) of one (b, h).
-template <int D>
+// One row block (128 query rows starting at rb * 128) of one (b, h). TRAIN
+// (the training forward, which also writes mu_v and the row statistics the
+// backward recomputes the weights from) contracts the weights as split bf16
+// pairs against bf16 V; otherwise they are rounded once to fp16 against fp16 V.
+template <int D, bool TRAIN>
 __device__ __forceinline__ void prefill_rows(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
@@ -178,7 +221,9 @@ __device__ __forceinline__ void prefill_rows(
       piece(i, which, idx);
       const int r = idx / (P::ROWB / 16);
       const int c16 = idx % (P::ROWB / 16);
-      *reinterpret_cast<i32x4*>(&kv_lds[buf][which][r * (which ? P::VSTR : P::LSTR) + c16 * 16]) = src[i];
+      // without TRAIN, V is staged as fp16 (the value MFMAs take fp16 weights)
+      const i32x4 val = (!TRAIN && which) ? bf16x8_to_f16x8(src[i]) : src[i];
+      *reinterpret_cast<i32x4*>(&kv_lds[buf][which][r * (which ? P::VSTR : P::LSTR) + c16 * 16]) = val;
     }
   };
 
@@ -193,6 +238,96 @@ __device__ __forceinline__ void prefill_rows(
   float bsum = 0.f;     // this lane's part of Bs
   f32x4 rinit = {0.f, 0.f, 0.f, 0.f};  // start of the rho . k accumulators: -rho_t . k_0
 
+  // Training forward, weights as split bf16 pairs: the reference c is
+  // rho_t . k_0 (taken on block 0), the row max moves lazily (by more than
+  // 2^8), and e and e (r - c) reach the value MFMAs as a bf16 high part plus
+  // the bf16 rounding of the remainder (four products per value tile), so the
+  // fp32 weights survive the contraction to about 2^-17: mu_v and the row
+  // statistics feed the gradients, where the 2^-12 of one fp16 rounding
+  // would use up most of the error bar.
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  auto contract_split = [&](int kb, f32x4 (&sc)[2], f32x4 (&rc)[2], const i16x4 (&vr)[P::DPL][2]) {
+    if (kb == 0) {
+      const float cref = __shfl(rc[0][0], c);  // key 0 sits in lane (0, c), slot 0
+      rinit = f32x4{-cref, -cref, -cref, -cref};
+#pragma unroll
+      for (int T2 = 0; T2 < 2; ++T2) rc[T2] -= cref;
+    }
+    float mx = -INFINITY;
+    const bool diag = kb * kKeys + kKeys - 1 > past + wrow0;
+    if (diag) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kb * kKeys + 16 * (e >> 2) + 4 * g + (e & 3);
+        mx = fmaxf(mx, key <= my_pos ? sc[e >> 2][e & 3] : -INFINITY);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[e >> 2][e & 3]);
+    }
+    mx *= sl;
+    // Lazy rescale: each lane checks its own 8 keys; the row max (two
+    // exchanges) is formed only when some lane exceeds the bound.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > m + kRescaleLog2;
+      const float mnew = need ? mx : m;
+      const float alpha = need ? exp2f(m - mnew) : 1.0f;
+      m = mnew;
+      lsum *= alpha;
+      bsum *= alpha;
+      float arow[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int j = 0; j < P::DPL; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accA[j][i] *= arow[i];
+          accC[j][i] *= arow[i];
+        }
+    }
+    float ev[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ev[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 2][e & 3], sl, -m));
+    if (diag) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kb * kKeys + 16 * (e >> 2) + 4 * g + (e & 3);
+        ev[e] = key <= my_pos ? ev[e] : 0.f;
+      }
+    }
+    uint32_t phw[4], plw[4], qhw[4], qlw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float e0 = ev[2 * u];
+      const float e1 = ev[2 * u + 1];
+      const float f0 = e0 * rc[u >> 1][(2 * u) & 3];
+      const float f1 = e1 * rc[u >> 1][(2 * u + 1) & 3];
+      lsum += e0 + e1;
+      bsum += f0 + f1;
+      const uint32_t ph = pack_bf16(e0, e1);
+      const uint32_t qh = pack_bf16(f0, f1);
+      phw[u] = ph;
+      qhw[u] = qh;
+      plw[u] = pack_bf16(e0 - bf16_lo(ph), e1 - bf16_hi(ph));
+      qlw[u] = pack_bf16(f0 - bf16_lo(qh), f1 - bf16_hi(qh));
+    }
+    const bf16x8 a_ph = as_bf16x8(phw[0], phw[1], phw[2], phw[3]);
+    const bf16x8 a_pl = as_bf16x8(plw[0], plw[1], plw[2], plw[3]);
+    const bf16x8 a_qh = as_bf16x8(qhw[0], qhw[1], qhw[2], qhw[3]);
+    const bf16x8 a_ql = as_bf16x8(qlw[0], qlw[1], qlw[2], qlw[3]);
+#pragma unroll
+    for (int j = 0; j < P::DPL; ++j) {
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vr[j][0], vr[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ph, vop, accA[j], 0, 0, 0);
+      accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pl, vop, accA[j], 0, 0, 0);
+      accC[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_qh, vop, accC[j], 0, 0, 0);
+      accC[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ql, vop, accC[j], 0, 0, 0);
+    }
+  };
+
   // Contracts key block kb (LDS buffer buf) into this wave's accumulators.
   auto contract = [&](int kb, int buf) {
     // ---- transposed scores: lane (g, c) holds row my_row, keys 16 T + 4 g + i.
@@ -202,8 +337,6 @@ __device__ __forceinline__ void prefill_rows(
     // the score MFMAs, then every V operand read, so the V reads are in flight
     // while the scores finish and the softmax runs, instead of each value
     // MFMA waiting on its own LDS round trip.
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     bf16x8 kop[2][P::KST];
 #pragma unroll
@@ -241,11 +374,10 @@ __device__ __forceinline__ void prefill_rows(
       vr[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * j + 16 * P::VSTR));
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kb == 0) {
-      const float cref = __shfl(rc[0][0], c);  // key 0 sits in lane (0, c), slot 0
-      rinit = f32x4{-cref, -cref, -cref, -cref};
-#pragma unroll
-      for (int T2 = 0; T2 < 2; ++T2) rc[T2] -= cref;
+
+    if constexpr (TRAIN) {
+      contract_split(kb, sc, rc, vr);
+      return;
     }
 
     // Raw scores; masked keys are -inf on the block that reaches past this
@@ -265,10 +397,17 @@ __device__ __forceinline__ void prefill_rows(
     }
     mx *= sl;
 
-    // Lazy rescale. The reference m of a row only has to bound every weight
-    // exp2(x - m) by 2^8, so each lane checks its own 8 keys; the row max
-    // (two exchanges) is formed only when some lane exceeds the bound.
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2)) {
+    // Reference moves (rare, wave-uniform branch): taken on the first block
+    // and whenever some lane's block max exceeds its row's reference max m by
+    // more than 2^3 (a key that now outweighs the reference key 8-fold).
+    //  - Lazy rescale: m only has to bound every weight exp2(x - m) by 2^8
+    //    (fp16 holds the weights), so it moves to the row max only past that.
+    //  - Probe reference: c moves to the running weighted mean of r (this
+    //    block included), so the products e (r - c), rounded once to fp16,
+    //    stay small next to the weights that dominate the row. The shift is
+    //    exact: Bs -> Bs - delta l and C -> C - delta A.
+    const bool moved = __builtin_amdgcn_ballot_w64(mx > m + kRefLog2) != 0;
+    if (moved) {
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool need = mx > m + kRescaleLog2;
@@ -290,8 +429,11 @@ __device__ __forceinline__ void prefill_rows(
         }
     }
 
-    // ---- weights e and e (r - c) as packed bf16 high parts and the bf16
-    // rounding of the remainders: the A operands of the value MFMAs
+    // ---- weights e and e (r - c), each rounded once to fp16 (toward zero):
+    // the A operands of the value MFMAs. l and Bs sum the rounded values, so
+    // the weights that reach A and C are exactly those of l and Bs, and the
+    // rounding only perturbs each weight by 2^-11 of itself instead of
+    // leaving A out of step with l.
     float ev[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ev[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 2][e & 3], sl, -m));
@@ -302,35 +444,52 @@ __device__ __forceinline__ void prefill_rows(
         ev[e] = key <= my_pos ? ev[e] : 0.f;
       }
     }
-    uint32_t phw[4], plw[4], qhw[4], qlw[4];
+    if (moved) {
+      float ltot = lsum, btot = bsum;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ltot += ev[e];
+        btot += ev[e] * rc[e >> 2][e & 3];
+      }
+      ltot += __shfl_xor(ltot, 16);
+      ltot += __shfl_xor(ltot, 32);
+      btot += __shfl_xor(btot, 16);
+      btot += __shfl_xor(btot, 32);
+      const float delta = btot / ltot;  // key 0 is visible to every row: ltot > 0
+      bsum -= delta * lsum;
+      rinit -= delta;
+#pragma unroll
+      for (int T2 = 0; T2 < 2; ++T2) rc[T2] -= delta;
+      float drow[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) drow[i] = __shfl(delta, 4 * g + i);
+#pragma unroll
+      for (int j = 0; j < P::DPL; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accC[j][i] = __builtin_fmaf(-drow[i], accA[j][i], accC[j][i]);
+    }
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    uint32_t pw[4], fw[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float e0 = ev[2 * u];
       const float e1 = ev[2 * u + 1];
-      const float f0 = e0 * rc[u >> 1][(2 * u) & 3];
-      const float f1 = e1 * rc[u >> 1][(2 * u + 1) & 3];
-      lsum += e0 + e1;
-      bsum += f0 + f1;
-      const uint32_t ph = pack_bf16(e0, e1);
-      const uint32_t qh = pack_bf16(f0, f1);
-      phw[u] = ph;
-      qhw[u] = qh;
-      plw[u] = pack_bf16(e0 - bf16_lo(ph), e1 - bf16_hi(ph));
-      qlw[u] = pack_bf16(f0 - bf16_lo(qh), f1 - bf16_hi(qh));
+      const f16x2 ph = pack_f16_rtz(e0, e1);
+      const f16x2 fh = pack_f16_rtz(e0 * rc[u >> 1][(2 * u) & 3], e1 * rc[u >> 1][(2 * u + 1) & 3]);
+      lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
+      bsum = __builtin_amdgcn_fdot2(fh, ones, bsum, false);
+      pw[u] = __builtin_bit_cast(uint32_t, ph);
+      fw[u] = __builtin_bit_cast(uint32_t, fh);
     }
-    const bf16x8 a_ph = as_bf16x8(phw[0], phw[1], phw[2], phw[3]);
-    const bf16x8 a_pl = as_bf16x8(plw[0], plw[1], plw[2], plw[3]);
-    const bf16x8 a_qh = as_bf16x8(qhw[0], qhw[1], qhw[2], qhw[3]);
-    const bf16x8 a_ql = as_bf16x8(qlw[0], qlw[1], qlw[2], qlw[3]);
+    const f16x8 a_p = as_f16x8(pw[0], pw[1], pw[2], pw[3]);
+    const f16x8 a_f = as_f16x8(fw[0], fw[1], fw[2], fw[3]);
 
-    // ---- value MFMAs
+    // ---- value MFMAs (V was staged as fp16)
 #pragma unroll
     for (int j = 0; j < P::DPL; ++j) {
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vr[j][0], vr[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-      accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ph, vop, accA[j], 0, 0, 0);
-      accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_pl, vop, accA[j], 0, 0, 0);
-      accC[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_qh, vop, accC[j], 0, 0, 0);
-      accC[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ql, vop, accC[j], 0, 0, 0);
+      const f16x8 vop = __builtin_bit_cast(f16x8, __builtin_shufflevector(vr[j][0], vr[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_p, vop, accA[j], 0, 0, 0);
+      accC[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_f, vop, accC[j], 0, 0, 0);
     }
   };
 
@@ -406,7 +565,7 @@ __device__ __forceinline__ void prefill_rows(
 // causal mask their key counts add up to the same total for every x, so all
 // workgroups carry equal work and the short early row blocks never form a
 // tail of their own.
-template <int D>
+template <int D, bool TRAIN>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
@@ -428,34 +587,34 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     h = (int)((L / npairs) % gridDim.y);
     b = (int)(L / (npairs * gridDim.y));
   }
-  prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
+  prefill_rows<D, TRAIN>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
                   scale_log2, nrb - 1 - x, h, b, kv_lds);
   if (x != nrb - 1 - x) {
     __syncthreads();
-    prefill_rows<D>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
+    prefill_rows<D, TRAIN>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
                     scale_log2, x, h, b, kv_lds);
   }
+}
+
+template <int D, bool TRAIN>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  const int nrb = (a.T + kRows - 1) / kRows;
+  dim3 grid((nrb + 1) / 2, a.H_q, a.B);  // row blocks paired heavy + light
+  hipLaunchKernelGGL((prefill_kernel<D, TRAIN>), grid, dim3(kThreads), 0, st,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
+                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v), a.seq_lens,
+                     a.past_lens, a.out, a.mu_out, static_cast<float4*>(a.stats), a.H_q, a.H_kv,
+                     a.G, a.T, a.S_max, a.scale * kLog2e);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
-  const int nrb = (a.T + kRows - 1) / kRows;
-  dim3 grid((nrb + 1) / 2, a.H_q, a.B);  // row blocks paired heavy + light
-  if (a.d == 64) {
-    hipLaunchKernelGGL((prefill_kernel<64>), grid, dim3(kThreads), 0, st,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
-                       static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                       a.seq_lens, a.past_lens, a.out, a.mu_out, static_cast<float4*>(a.stats), a.H_q,
-                       a.H_kv, a.G, a.T, a.S_max, a.scale * kLog2e);
-  } else {
-    hipLaunchKernelGGL((prefill_kernel<128>), grid, dim3(kThreads), 0, st,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
-                       static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                       a.seq_lens, a.past_lens, a.out, a.mu_out, static_cast<float4*>(a.stats), a.H_q,
-                       a.H_kv, a.G, a.T, a.S_max, a.scale * kLog2e);
-  }
-  return hipGetLastError();
+  const bool train = a.mu_out != nullptr;
+  if (a.d == 64)
+    return train ? launch_prefill_t<64, true>(a, st) : launch_prefill_t<64, false>(a, st);
+  return train ? launch_prefill_t<128, true>(a, st) : launch_prefill_t<128, false>(a, st);
 }
 
 }  // namespace parallax

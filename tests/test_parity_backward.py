@@ -159,7 +159,17 @@ def test_training_forward_outputs():
     dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     plain = pa.prefill(dev["q"], dev["rho"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"])
     torch.cuda.synchronize()
-    assert np.array_equal(out, plain.cpu().numpy())  # same kernel, extra outputs only
+    # The training forward contracts split bf16 weights, the inference prefill
+    # fp16 ones: both outputs within the bar of the oracle, the training one
+    # to the split weights' precision.
+    ref = oracle.oracle_prefill_full(inp["q"], inp["rho"], inp["k"], inp["v"], inp["seq_lens"],
+                                     inp["scale"])
+    plain = plain.cpu().numpy()
+    for (b, h), r in ref.items():
+        n = int(inp["seq_lens"][b])
+        den = np.abs(r[:n]).max(axis=-1)
+        assert (np.abs(out[b, h, :n] - r[:n]).max(axis=-1) / den).max() < 1e-4
+        assert (np.abs(plain[b, h, :n] - r[:n]).max(axis=-1) / den).max() < TOL
     q, k, v, rho = (inp[x].double().numpy() for x in ("q", "k", "v", "rho"))
     lens = inp["seq_lens"].tolist()
     G = w.H_q // w.H_kv

@@ -112,6 +112,13 @@ def test_negative_and_zero_scale(scale):
     check(replace_shape(SMALL, scale=scale))
 
 
+@pytest.mark.parametrize("rho_std,scale", [(1.0, 1.0), (1.0, 8.0)])
+def test_strong_probe(rho_std, scale):
+    """Probes 20x the workload's, with a long past: the fp16 value weights are
+    most exposed where the covariance correction dominates the output."""
+    check(replace_shape(SMALL, rho_std=rho_std, scale=scale, past=1500, T=130))
+
+
 def test_group_sizes_and_head_dim_64():
     check(replace_shape(SMALL, H_q=8, H_kv=2))
     check(replace_shape(SMALL, d=64, q_std=64 ** -0.25, k_std=64 ** -0.25))

@@ -118,6 +118,16 @@ def test_sharp_softmax():
     check(replace_shape(SMALL, scale=8.0))
 
 
+@pytest.mark.parametrize("rho_std,scale", [(0.5, 1.0), (1.0, 1.0), (1.0, 8.0)])
+def test_strong_probe(rho_std, scale):
+    """Probes 10-20x the workload's: the covariance correction dominates the
+    output, and with a sharp softmax a few keys far from the probe reference
+    carry the weight. The value contraction's fp16 weights are most exposed
+    here."""
+    w = replace_shape(SMALL, rho_std=rho_std, scale=scale, T=384)
+    check(w, seq_lens=[384, 301])
+
+
 def test_unscaled_dot_reading():
     check(replace_shape(SMALL, scale=128 ** -0.5))
 
