@@ -27,9 +27,9 @@
  *  - Tensor pointers are DEVICE pointers to dense row-major arrays (last
  *    dimension contiguous) on the current HIP device; they must be 16-byte
  *    aligned. The caller owns every buffer; the library never allocates or
- *    frees memory, never synchronises, and keeps no mutable global state (a
- *    lazily filled, thread-safe cache of per-device compute-unit counts is the
- *    only global).
+ *    frees memory, never synchronises, and keeps no mutable global state
+ *    besides a lazily filled, thread-safe cache of per-device compute-unit
+ *    counts and the per-device scratch of parallax_decode_noalloc.
  *  - Inputs are read only. Outputs are written in full (every element), except
  *    the K/V caches of parallax_qkvr_projection, of which only the projected
  *    rows are written.
@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 5
+#define PARALLAX_ABI_VERSION 6
 
 typedef enum {
   PARALLAX_OK = 0,
@@ -69,7 +69,8 @@ typedef enum {
   PARALLAX_ERR_UNSUPPORTED = 3,  /* d, G, dtype or size outside what is built */
   PARALLAX_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
   PARALLAX_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required */
-  PARALLAX_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+  PARALLAX_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed */
+  PARALLAX_ERR_TOO_LARGE = 7     /* beyond the built-in scratch of parallax_decode_noalloc */
 } parallax_status_t;
 
 typedef enum { PARALLAX_BF16 = 0, PARALLAX_F32 = 1 } parallax_dtype_t;
@@ -134,6 +135,39 @@ parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_
                                   int B, int H_q, int H_kv, int d, int S_max, float scale,
                                   parallax_dtype_t dtype, int num_splits, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Bytes of the scratch array parallax_decode_noalloc keeps on each device,
+ * and the part of it that holds the arrival counters. */
+#define PARALLAX_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define PARALLAX_NOALLOC_COUNTER_BYTES (256u << 10)
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): parallax_decode (same arguments, checks, result and single
+ * fused launch, minus the workspace) with the partial records and arrival
+ * counters in a scratch array the library holds on each device it runs on,
+ * from the library's load until the process ends:
+ * PARALLAX_NOALLOC_SCRATCH_BYTES (32 MiB), of which
+ * PARALLAX_NOALLOC_COUNTER_BYTES (256 KiB) hold the counters.
+ *  - Limit: the resolved plan's records, B * H_q * num_splits * (2 d + 4) * 4
+ *    bytes, within the scratch past the counters (33,292,288 bytes; this
+ *    also keeps B * H_q within the 65,536 counters). Beyond it,
+ *    PARALLAX_ERR_TOO_LARGE and nothing is launched. A one-split plan (no
+ *    records, no counters) has no limit and does not touch the scratch.
+ *  - The first call on a device (that device current) looks up the array's
+ *    address and clears its counters with a small kernel on `stream`; every
+ *    call returns them to zero.
+ *  - Every call on one device shares that device's array: calls that
+ *    overlap on a device (different streams without ordering, or several
+ *    host threads) race and give wrong results. Order them.
+ *  - Nothing is allocated: no hipMalloc, hipFree or allocating library call.
+ */
+parallax_status_t parallax_decode_noalloc(const void* q, const void* rho, const void* k_cache,
+                                          const void* v_cache, const int32_t* seq_lens,
+                                          float* out, int B, int H_q, int H_kv, int d, int S_max,
+                                          float scale, parallax_dtype_t dtype, int num_splits,
+                                          void* stream);
 
 /*
  * First phase of decode: streams every valid K/V row once and writes one

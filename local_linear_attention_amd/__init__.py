@@ -9,6 +9,7 @@ Functions mirror the C entry points:
 
 * ``decode_plan``, ``decode_workspace_size``
 * ``decode`` (one shot), ``decode_partial`` + ``decode_combine`` (two phases)
+* ``decode_noalloc`` (one shot, with the library's built-in scratch instead of a workspace)
 * ``prefill`` (causal), ``prefill_chunked`` (causal against an existing cache)
 * ``decode_tokens`` (the chunked result for a few new tokens, by the split-KV decode)
 * ``prefill_train`` + ``prefill_backward`` (gradients of the causal prefill)
@@ -25,7 +26,8 @@ import torch
 
 __all__ = [
     "ParallaxError", "lib", "library_path", "abi_version", "status_string", "decode_plan",
-    "decode_workspace_size", "decode", "decode_partial", "decode_combine", "prefill",
+    "decode_workspace_size", "decode", "decode_partial", "decode_combine", "decode_noalloc",
+    "prefill",
     "prefill_chunked", "decode_tokens", "prefill_train", "prefill_backward_workspace_size",
     "prefill_backward",
     "qkvr_projection", "read_probe",
@@ -43,6 +45,7 @@ STATUS = {
     4: "PARALLAX_ERR_MISALIGNED",
     5: "PARALLAX_ERR_WORKSPACE",
     6: "PARALLAX_ERR_HIP",
+    7: "PARALLAX_ERR_TOO_LARGE",
 }
 _BF16, _F32 = 0, 1
 
@@ -50,7 +53,7 @@ EXPORTED_SYMBOLS = (
     "parallax_abi_version", "parallax_status_string", "parallax_decode_plan",
     "parallax_decode_workspace_size", "parallax_decode", "parallax_decode_partial",
     "parallax_decode_combine", "parallax_prefill", "parallax_prefill_chunked",
-    "parallax_decode_tokens",
+    "parallax_decode_tokens", "parallax_decode_noalloc",
     "parallax_prefill_train", "parallax_prefill_backward_workspace_size",
     "parallax_prefill_backward", "parallax_qkvr_projection", "parallax_read_probe",
 )
@@ -98,6 +101,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.parallax_decode.argtypes = dec
     L.parallax_decode_partial.restype = i
     L.parallax_decode_partial.argtypes = dec
+    L.parallax_decode_noalloc.restype = i
+    L.parallax_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     L.parallax_decode_combine.restype = i
     L.parallax_decode_combine.argtypes = [vp, vp, i, i, i, i, i, i, vp, sz, vp]
     L.parallax_prefill.restype = i
@@ -231,6 +236,20 @@ def decode(q, rho, k_cache, v_cache, seq_lens, scale: float, *, num_splits: int 
             seq_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, S_max, float(scale),
             _dtype_code(q), int(num_splits), ws.data_ptr(), ws_bytes, _stream_ptr(q.device)),
             "parallax_decode")
+    return out
+
+
+def decode_noalloc(q, rho, k_cache, v_cache, seq_lens, scale: float, *, num_splits: int = 0,
+                   out=None):
+    """Parallax decode with the library's built-in per-device scratch instead of a
+    workspace (see parallax_decode_noalloc); returns out [B, H_q, d] fp32."""
+    B, H_q, H_kv, d, S_max = _decode_shapes(q, rho, k_cache, v_cache, seq_lens)
+    out = _out_tensor(out, (B, H_q, d), q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().parallax_decode_noalloc(
+            q.data_ptr(), rho.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            seq_lens.data_ptr(), out.data_ptr(), B, H_q, H_kv, d, S_max, float(scale),
+            _dtype_code(q), int(num_splits), _stream_ptr(q.device)), "parallax_decode_noalloc")
     return out
 
 

@@ -107,7 +107,7 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
                                const int32_t* seq_lens, float* out, bool need_out, int B,
                                int H_q, int H_kv, int d, int S_max, float scale,
                                parallax_dtype_t dtype, int num_splits, void* ws,
-                               size_t ws_bytes, Checked* c) {
+                               size_t ws_bytes, Checked* c, bool check_ws = true) {
   if (!q || !rho || !k || !v || !seq_lens) return PARALLAX_ERR_NULL_POINTER;
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || S_max <= 0 || num_splits < 0 ||
       H_q % H_kv != 0)
@@ -130,13 +130,13 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   if ((direct || need_out) && !out) return PARALLAX_ERR_NULL_POINTER;
   if (out && !aligned16(out)) return PARALLAX_ERR_MISALIGNED;
   const size_t need = workspace_bytes_for(B, H_q, d, ns);
-  if (need > 0) {
+  if (need > 0 && check_ws) {
     if (!ws || ws_bytes < need) return PARALLAX_ERR_WORKSPACE;
     if (!aligned16(ws)) return PARALLAX_ERR_MISALIGNED;
   }
   c->ws_need = need;
   void* counters = nullptr;
-  if (need > 0 && need_out)
+  if (need > 0 && need_out && ws)
     counters = static_cast<char*>(ws) + records_bytes(B, H_q, d, ns);
   c->a = parallax::DecodeArgs{q, rho, k, v, seq_lens, nullptr, out, ws, counters, B, H_q, H_kv,
                               G, d, S_max, ns, chunk, 1, scale, dtype == PARALLAX_F32};
@@ -146,6 +146,42 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
 parallax_status_t hip_status(hipError_t e) { return e == hipSuccess ? PARALLAX_OK : PARALLAX_ERR_HIP; }
 
 }  // namespace
+
+namespace parallax {
+
+// parallax_decode with the partial records and arrival counters in a scratch
+// region that `get_scratch` supplies: counters at its start (counter_bytes),
+// records after them. Every argument check runs first; `get_scratch` is
+// called (and may launch its own set-up on `stream`) only when the call will
+// launch, and only when the plan has several splits. PARALLAX_ERR_TOO_LARGE
+// when the plan's records or counters exceed their part of the region.
+parallax_status_t decode_in_scratch(const void* q, const void* rho, const void* k_cache,
+                                    const void* v_cache, const int32_t* seq_lens, float* out, int B,
+                                    int H_q, int H_kv, int d, int S_max, float scale,
+                                    parallax_dtype_t dtype, int num_splits, ScratchFn get_scratch,
+                                    size_t scratch_bytes, size_t counter_bytes, void* stream) {
+  try {
+    Checked c;
+    parallax_status_t st = check_decode(q, rho, k_cache, v_cache, seq_lens, out, true, B, H_q, H_kv,
+                                        d, S_max, scale, dtype, num_splits, nullptr, 0, &c, false);
+    if (st != PARALLAX_OK) return st;
+    if (c.ws_need > 0) {
+      if ((size_t)B * H_q * sizeof(uint32_t) > counter_bytes ||
+          records_bytes(B, H_q, d, c.a.num_splits) > scratch_bytes - counter_bytes)
+        return PARALLAX_ERR_TOO_LARGE;
+      void* base = nullptr;
+      st = get_scratch(static_cast<hipStream_t>(stream), &base);
+      if (st != PARALLAX_OK) return st;
+      c.a.counters = base;
+      c.a.ws = static_cast<char*>(base) + counter_bytes;
+    }
+    return hip_status(launch_decode_partial(c.a, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return PARALLAX_ERR_HIP;
+  }
+}
+
+}  // namespace parallax
 
 extern "C" {
 
@@ -160,6 +196,8 @@ const char* parallax_status_string(parallax_status_t s) {
     case PARALLAX_ERR_MISALIGNED: return "PARALLAX_ERR_MISALIGNED: a tensor pointer is not 16-byte aligned";
     case PARALLAX_ERR_WORKSPACE: return "PARALLAX_ERR_WORKSPACE: workspace missing or too small";
     case PARALLAX_ERR_HIP: return "PARALLAX_ERR_HIP: HIP runtime or launch failure";
+    case PARALLAX_ERR_TOO_LARGE:
+      return "PARALLAX_ERR_TOO_LARGE: the sizes exceed the built-in scratch of parallax_decode_noalloc";
   }
   return "unknown parallax status";
 }

@@ -2,7 +2,10 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "parallax.h"
 
 namespace parallax {
 
@@ -79,6 +82,16 @@ struct ProjArgs {
 inline int decode_heads_per_workgroup(int G) { return G > 4 ? 8 : 4; }
 
 hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st);
+
+// parallax_decode with its partial records and arrival counters in a
+// scratch region supplied by `get_scratch` after every argument check has
+// passed (defined in api.cpp; used by the allocation-free entry point).
+typedef parallax_status_t (*ScratchFn)(hipStream_t stream, void** base);
+parallax_status_t decode_in_scratch(const void* q, const void* rho, const void* k_cache,
+                                    const void* v_cache, const int32_t* seq_lens, float* out, int B,
+                                    int H_q, int H_kv, int d, int S_max, float scale,
+                                    parallax_dtype_t dtype, int num_splits, ScratchFn get_scratch,
+                                    size_t scratch_bytes, size_t counter_bytes, void* stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st);

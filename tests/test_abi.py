@@ -16,7 +16,7 @@ import local_linear_attention_amd as pa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "parallax.h")
 
-OK, NULLP, SHAPE, UNSUP, MISAL, WS, HIP = range(7)
+OK, NULLP, SHAPE, UNSUP, MISAL, WS, HIP, TOO_LARGE = range(8)
 BF16, F32 = 0, 1
 P = 0x10000  # 16-byte aligned fake device address
 
@@ -38,7 +38,7 @@ def header_functions():
 
 def test_header_symbols_exported(L):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert set(names) == set(pa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(L, n), n
@@ -110,6 +110,32 @@ def test_decode_argument_errors(L, fn):
     assert _decode(L, fn, ws_bytes=100) == WS
     assert _decode(L, fn, ws=P + 4) == MISAL
     assert _decode(L, fn, out=P + 4) == MISAL
+
+
+def _noalloc(L, q=P, rho=P, k=P, v=P, lens=P, out=P, B=2, Hq=4, Hkv=2, d=128, S=512, scale=1.0,
+             dtype=BF16, ns=2):
+    return L.parallax_decode_noalloc(q, rho, k, v, lens, out, B, Hq, Hkv, d, S, scale, dtype, ns,
+                                     None)
+
+
+def test_decode_noalloc_argument_errors(L):
+    """Every check runs on the host before the scratch is set up or anything is
+    launched (an explicit split count needs no device query)."""
+    assert _noalloc(L, q=0) == NULLP
+    assert _noalloc(L, out=0) == NULLP
+    assert _noalloc(L, B=0) == SHAPE
+    assert _noalloc(L, Hq=3, Hkv=2) == SHAPE
+    assert _noalloc(L, ns=-1) == SHAPE
+    assert _noalloc(L, scale=float("nan")) == SHAPE
+    assert _noalloc(L, d=96) == UNSUP
+    assert _noalloc(L, dtype=7) == UNSUP
+    assert _noalloc(L, k=P + 8) == MISAL
+    assert _noalloc(L, out=P + 4) == MISAL
+    # records of 64 x 16 heads x 32 splits x 260 floats: 34 MB, past the 32 MiB scratch
+    assert _noalloc(L, B=64, Hq=16, Hkv=8, S=32768, ns=32) == TOO_LARGE
+    # d = 64: 2048 x 64 heads x 2 splits x 132 floats = 138 MB
+    assert _noalloc(L, B=2048, Hq=64, Hkv=8, d=64, S=256, ns=2) == TOO_LARGE
+    assert "scratch" in pa.status_string(TOO_LARGE)
 
 
 def test_decode_out_required(L):
