@@ -452,22 +452,31 @@ def qkvr_projection(x, w, H_q: int, H_kv: int, d: int, *, k_cache=None, v_cache=
     (allocated, zero-filled, with S_max = T when not given). See
     parallax_qkvr_projection.
     """
-    _dev_tensor(x, "x")
-    _dev_tensor(w, "w")
+    # shapes first (the caches' rows decide where the kernel writes), devices after
     if x.dim() != 3 or w.dim() != 2 or w.shape[1] != x.shape[2] or \
             w.shape[0] != (2 * H_q + 2 * H_kv) * d:
         raise ValueError("x is [B, T, d_model] and w [(2 H_q + 2 H_kv) d, d_model]")
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise TypeError("x and w must be bf16")
     B, T, d_model = x.shape
+    if (k_cache is None) != (v_cache is None):
+        raise ValueError("pass both k_cache and v_cache, or neither")
     if k_cache is None:
         S = T if S_max is None else int(S_max)
         k_cache = torch.zeros((B, H_kv, S, d), dtype=torch.bfloat16, device=x.device)
         v_cache = torch.zeros_like(k_cache)
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _dev_tensor(t, name)
-        if t.shape[:2] != (B, H_kv) or t.shape[3] != d or t.dtype != torch.bfloat16:
+        if t.dim() != 4 or t.shape[:2] != (B, H_kv) or t.shape[3] != d or \
+                t.dtype != torch.bfloat16:
             raise ValueError(f"{name} must be bf16 [B, H_kv, S_max, d]")
+    # the kernel writes both caches at k_cache's row stride: V must have the same rows
+    if v_cache.shape != k_cache.shape:
+        raise ValueError(f"v_cache {tuple(v_cache.shape)} must have k_cache's shape "
+                         f"{tuple(k_cache.shape)}")
+    if S_max is not None and int(S_max) != k_cache.shape[2]:
+        raise ValueError(f"S_max={S_max} disagrees with the caches' {k_cache.shape[2]} rows")
+    for name, t in (("x", x), ("w", w), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name)
     if past_lens is not None:
         _dev_tensor(past_lens, "past_lens")
         if past_lens.dtype != torch.int32 or past_lens.shape != (B,):

@@ -576,6 +576,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
   __syncthreads();
   if (!s_last) return;
+  // The merging workgroup acquires at agent scope before it reads the other
+  // workgroups' records: stale lines of this XCD's caches are invalidated.
+  // Only this one workgroup per stream pays for it.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int nsv = (n + chunk - 1) / chunk;
   for (int idx = tid; idx < Gw * D / 2; idx += 256) {  // (head, pair of dims)
     const int h = idx / (D / 2);

@@ -5,7 +5,7 @@
 // Linear Attention", "The Core Insight: Covariance Correction" and
 // "Architecture-Optimizer Codesign", the W_R projection; paper page
 // "Parallax: Parameterized Local Linear Attention for Language Modeling",
-// "Abstract": an extra query-like projector). One GEMM produces all four
+// "Abstract": a second projection of the input, used like a query). One GEMM produces all four
 // projections of x, written in bf16 (round to nearest even) straight into the
 // layouts the attention kernels read:
 //

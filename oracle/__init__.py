@@ -14,8 +14,9 @@ Sources the oracle follows (page titles and sections):
   minus the key/value covariance applied to a probe vector rho, and rho is a
   learned projection of the input.
 * "Parallax: Parameterized Local Linear Attention for Language Modeling"
-  (paper detail page), "Abstract": rho is a query-like projector probing the KV
-  covariance; softmax attention is the local-constant (Nadaraya-Watson)
+  (paper detail page), "Abstract": rho acts like a second query, dotted with
+  the keys, and selects which direction of the key/value covariance corrects
+  the output; softmax attention is the local-constant (Nadaraya-Watson)
   estimate that local linear attention improves on.
 * Same blog post, section "Context: Why 'Softmax' is Not Enough": softmax
   attention is a Nadaraya-Watson estimator (local constant).

@@ -17,8 +17,8 @@ it may see, following the explicit definition and not any streaming form:
 3. Sigma_KV = sum_i w_i (v_i - mu_v)(k_i - mu_k)^T, a d_v x d_k matrix formed
    entry by entry through one matrix product.
    [blog, section "The Core Insight: Covariance Correction", output equation;
-   paper page "Abstract": the extra projector is query-like and probes the KV
-   covariance.] Readings taken where the pages are silent: rho lives in key
+   paper page "Abstract": rho is a second, query-like projection whose dot
+   with the keys selects the covariance correction.] Readings taken where the pages are silent: rho lives in key
    space (it is dotted with keys, as a query is), so the matrix is
    value-rows x key-columns; it is centred at the softmax-weighted means; its
    weights are the same softmax weights, summing to one.

@@ -53,3 +53,22 @@ def test_prefill_and_chunk_outputs_checked():
         with pytest.raises(ValueError):
             fn(p["q"], p["rho"], p["k"], p["v"], zero, lens, p["scale"],
                out=torch.empty((1, 2, 64, 64), device="cuda"))
+
+
+def test_projection_cache_shapes_rejected_before_launch():
+    """The projection writes K and V rows at k_cache's row stride: a v_cache with
+    other rows, a lone cache, or an S_max the caches disagree with is refused
+    (checked before any device work, so this runs on the CPU)."""
+    B, T, C, Hq, Hkv, d = 1, 8, 64, 2, 1, 64
+    x = torch.zeros((B, T, C), dtype=torch.bfloat16)
+    w = torch.zeros(((2 * Hq + 2 * Hkv) * d, C), dtype=torch.bfloat16)
+    k = torch.zeros((B, Hkv, 16, d), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="v_cache"):
+        pa.qkvr_projection(x, w, Hq, Hkv, d, k_cache=k,
+                           v_cache=torch.zeros((B, Hkv, 12, d), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="both"):
+        pa.qkvr_projection(x, w, Hq, Hkv, d, k_cache=k)
+    with pytest.raises(ValueError, match="S_max"):
+        pa.qkvr_projection(x, w, Hq, Hkv, d, k_cache=k, v_cache=k.clone(), S_max=32)
+    with pytest.raises(ValueError, match="GPU tensor"):  # consistent shapes reach the device check
+        pa.qkvr_projection(x, w, Hq, Hkv, d, k_cache=k, v_cache=k.clone(), S_max=16)
