@@ -1,23 +1,35 @@
 """Benchmark of the Parallax forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|main]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|main|prefill]
+    python bench.py --only NAME        # one workload alone (for profiling)
 
 A step is one pass of the decode hot path (one launch of the split-KV decode
 kernel, whose last workgroup per stream merges the partial states) over one
-batch of the GQA decode workload (B=8, H_q=16,
-H_kv=8, d=128, 4096 keys per sequence, bf16). The KV cache is held in 8
-copies in HBM (1.07 GB) and step i reads copy i mod 8, so no step finds its
-134 MB stream in the 256 MB Infinity Cache left there by the previous one.
-K timed steps are bracketed by device synchronisations; `value` is the KV
-stream (algorithmic bytes: every valid K and V row once) divided by the
-mean step time. A step is a single kernel launch, so a pair of HIP events on
-the launch stream around the timed region, divided by K, gives the kernel's
-average launch duration for the `roofline` object. The other workloads (single-head fp32, ragged batch,
-128K-context split-KV decode, causal prefill) are timed the same way, briefly,
-and reported under "workloads", with a chunked prefill (1024 new rows after
-3072 cached tokens), the GQA decode shape at 64 query heads on 8 KV heads, and
-multi-token decode (2, 3 and 4 new tokens per sequence at the GQA decode shape). The `cpu_baseline` leg times the fp64 oracle
-on a bounded sample of the same GQA decode workload on the host cores.
+batch of the GQA decode workload (B=8, H_q=16, H_kv=8, d=128, 4096 keys per
+sequence, bf16). The KV cache is held in 8 copies in HBM (1.07 GB) and step i
+reads copy i mod 8, so no step finds its 134 MB stream in the 256 MB Infinity
+Cache left there by the previous one. K timed steps are bracketed by device
+synchronisations; `value` is the KV stream (algorithmic bytes: every valid K
+and V row once) divided by the mean step time. A step is a single kernel
+launch, so a pair of HIP events on the launch stream around the timed region,
+divided by K, gives the kernel's average launch duration for the `roofline`
+object.
+
+Every workload (the main one included) also reports the distribution of 100
+single launches, each inside its own pair of HIP events on the launch stream
+(median, p10, p90). Workloads that read their inputs from one copy (no
+rotation) write a 512 MB scratch buffer before each of those launches, outside
+the event pair, so that no launch finds its inputs in the L2 or the Infinity
+Cache. `traffic` per workload comes from the committed rocprofv3 counter
+summaries (FETCH_SIZE and WRITE_SIZE, calibrated) while the kernel sources
+they were taken on are unchanged.
+
+Workloads: the GQA decode line (also at head dim 64), single-head fp32,
+ragged batch, 128K-context split-KV decode, 64 query heads on 8 KV heads,
+multi-token decode (2, 3 and 4 new tokens), causal prefill, chunked prefill
+(1024 new rows after 3072 cached tokens), the prefill backward and the fused
+q/k/v/rho projection. The `cpu_baseline` leg times the fp64 oracle on a
+bounded sample of the GQA decode workload on the host cores.
 
 One JSON line is printed at the end.
 """
@@ -47,27 +59,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
-    """Digest of the decode kernel sources (ties counter figures to a build)."""
+KERNEL_SOURCES = {
+    # profile file prefix -> the sources its kernel is built from
+    "decode_partial": ("decode.hip", "device_common.h"),
+    "prefill": ("prefill.hip", "device_common.h"),
+}
+
+
+def kernel_source_digest(prefix: str = "decode_partial") -> str:
+    """Digest of a kernel's sources (ties counter figures to a build)."""
     h = hashlib.sha256()
-    for f in ("decode.hip", "device_common.h"):
+    for f in KERNEL_SOURCES[prefix]:
         with open(os.path.join(ROOT, "local_linear_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per partial-kernel launch from the committed counter summary.
+def read_traffic(workload: str, prefix: str = "decode_partial"):
+    """HBM bytes per kernel launch from the committed counter summary
+    profiles/<prefix>_<workload>_pmc.md.
 
     Returns None when there is no summary or the kernel source changed since
     the counters were taken.
     """
-    path = os.path.join(PROFILE_DIR, f"decode_partial_{workload}_pmc.md")
+    path = os.path.join(PROFILE_DIR, f"{prefix}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
-    if not m or m.group(1) != kernel_source_digest():
+    if not m or m.group(1) != kernel_source_digest(prefix):
         return None
     vals = {}
     for key in ("fetch_bytes_per_launch", "write_bytes_per_launch"):
@@ -76,6 +96,59 @@ def read_traffic(workload: str):
             return None
         vals[key] = float(mm.group(1))
     return vals
+
+
+def traffic_entry(workload: str, algorithmic_bytes: float, prefix: str = "decode_partial"):
+    """The `traffic` fields of a workload entry (None when not measured on
+    these sources)."""
+    t = read_traffic(workload, prefix)
+    if t is None:
+        return {"traffic": None}
+    tot = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+    return {"traffic": int(tot), "traffic_fetch_bytes": int(t["fetch_bytes_per_launch"]),
+            "traffic_write_bytes": int(t["write_bytes_per_launch"]),
+            "fetch_over_algorithmic": round(t["fetch_bytes_per_launch"] / algorithmic_bytes, 4)}
+
+
+class Flusher:
+    """Writes a 512 MB scratch buffer (more than the 256 MB Infinity Cache and
+    every L2), so that the launch after it reads its inputs from HBM."""
+
+    def __init__(self):
+        import torch
+
+        self.buf = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(float(self.i & 7))
+
+
+def launch_stats(launch, n=100, warmup=3, flush=None):
+    """Per-launch durations: n single launches, each inside its own pair of HIP
+    events on the current stream (the one every launch here uses), with an
+    optional cache flush before each, outside the pair. Returns median, p10,
+    p90 and mean in microseconds."""
+    import numpy as np
+    import torch
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (e0, e1) in enumerate(ev):
+        if flush is not None:
+            flush()
+        e0.record()
+        launch(i)
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+    return {"n": n, "median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+            "p90_us": float(np.percentile(t, 90)), "mean_us": float(t.mean()),
+            "flushed": flush is not None}
 
 
 class DecodeRunner:
@@ -99,7 +172,7 @@ class DecodeRunner:
             ks.append(inp["k_cache"].clone())
             vs.append(inp["v_cache"].clone())
         self.ks, self.vs = ks, vs
-        self.ns, self.chunk = pa.decode_plan(w.B, w.H_q, w.H_kv, w.S_max, num_splits)
+        self.ns, self.chunk = pa.decode_plan(w.B, w.H_q, w.H_kv, w.d, w.S_max, num_splits)
         ws_bytes = max(pa.decode_workspace_size(w.B, w.H_q, w.d, self.ns), 16)
         self.ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device=dev)
         self.out = torch.empty((w.B, w.H_q, w.d), dtype=torch.float32, device=dev)
@@ -167,8 +240,40 @@ class DecodeRunner:
         t1 = time.perf_counter()
         return (t1 - t0) / steps, ev0.elapsed_time(ev1) / steps / 1e3
 
+    def launches(self, flush=None):
+        """Per-launch statistics (rotating over the cache copies)."""
+        return launch_stats(self.step, flush=flush)
 
-def bench_prefill(w, steps, warmup, seed=None, keep=None):
+
+def bench_decode(w, nbuf, steps, warmup, flush=None, read_ref=False, shape=None):
+    """A decode workload: back-to-back launches (wall and event span per
+    step) and the per-launch distribution; with `read_ref`, the plain read of
+    the same bytes."""
+    import torch
+
+    r = DecodeRunner(w, nbuf=nbuf)
+    s, p = r.run(steps, warmup)
+    res = {"us_per_step": s * 1e6, "kernel_us": p * 1e6, "kv_bytes": r.kv_bytes,
+           "GB_per_s": r.kv_bytes / p / 1e9,
+           "pct_of_hbm_peak": 100 * r.kv_bytes / p / 1e9 / HBM_PEAK_GBS,
+           "num_splits": r.ns, "chunk": r.chunk, "steps": steps,
+           "dtype": "f32" if w.dtype == torch.float32 else "bf16",
+           "launches": r.launches(flush=flush)}
+    res["pct_of_hbm_peak_median"] = 100 * r.kv_bytes / (res["launches"]["median_us"] * 1e-6) \
+        / 1e9 / HBM_PEAK_GBS
+    if shape is not None:
+        res["shape"] = shape
+    if read_ref and all(n == w.S_max for n in r.lens):
+        rs = r.read_probe(steps, warmup)
+        res["read_reference_us"] = rs * 1e6
+        res["decode_over_read"] = round(rs / p, 4)
+    res.update(traffic_entry(w.name, r.kv_bytes))
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(w, steps, warmup, seed=None, keep=None, flush=None):
     """Causal prefill per step. With `keep` (a dict), the inputs and the last
     output stay there for the oracle's timing leg."""
     import torch
@@ -184,31 +289,44 @@ def bench_prefill(w, steps, warmup, seed=None, keep=None):
     args = (inp["q"].data_ptr(), inp["rho"].data_ptr(), inp["k"].data_ptr(), inp["v"].data_ptr(),
             inp["seq_lens"].data_ptr(), out.data_ptr(), w.B, w.H_q, w.H_kv, w.d, w.T,
             inp["k"].shape[2], float(inp["scale"]), 0, stream)
-    for _ in range(warmup):
+
+    def one(_i=0):
         if L.parallax_prefill(*args) != 0:
             raise RuntimeError("prefill failed")
+
+    for _ in range(warmup):
+        one()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(steps):
-        L.parallax_prefill(*args)
+        one()
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = ev0.elapsed_time(ev1) / steps / 1e3
+    lst = launch_stats(one, flush=flush)
     if keep is not None:
         keep.update(inp=inp, out=out)
     # algorithmic work: q.k, rho.k, e.v and (e r).v over the causal half, 2 d flops each
     flops = 8.0 * w.d * (w.T * (w.T + 1) / 2) * w.B * w.H_q
-    return {"us_per_step": (t1 - t0) / steps * 1e6, "kernel_us": kern * 1e6,
-            "algorithmic_tflop": flops / 1e12, "tflops": flops / kern / 1e12,
-            "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
+    # algorithmic bytes: q, rho, K, V read once (bf16), out written once (fp32)
+    io = (2 * w.B * w.H_q * w.T * w.d + 2 * w.B * w.H_kv * w.T * w.d) * 2 \
+        + w.B * w.H_q * w.T * w.d * 4
+    res = {"us_per_step": (t1 - t0) / steps * 1e6, "kernel_us": kern * 1e6,
+           "algorithmic_tflop": flops / 1e12, "tflops": flops / kern / 1e12,
+           "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+           "launches": lst,
+           "mfma_util_median": flops / (lst["median_us"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+           "algorithmic_io_bytes": io,
+           "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
+    res.update(traffic_entry(w.name, io, prefix="prefill"))
+    return res
 
 
-def bench_backward(w, steps, warmup, seed=None):
+def bench_backward(w, steps, warmup, seed=None, flush=None):
     """Causal-prefill backward (prep + dq/drho + dk/dv launches) per step, and
     the training forward that saves mu_v and the row statistics."""
     import torch
@@ -238,9 +356,11 @@ def bench_backward(w, steps, warmup, seed=None):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / steps / 1e3
 
-    t_fwd = timed(lambda: pa.prefill_train(*args, inp["scale"]))
-    t_bwd = timed(lambda: pa.prefill_backward(*args, out, mu, stats, dout, inp["scale"],
-                                              workspace=ws))
+    fwd = lambda _i=0: pa.prefill_train(*args, inp["scale"])
+    bwd = lambda _i=0: pa.prefill_backward(*args, out, mu, stats, dout, inp["scale"], workspace=ws)
+    t_fwd = timed(fwd)
+    t_bwd = timed(bwd)
+    lst = launch_stats(bwd, n=30, flush=flush)
     pairs = w.T * (w.T + 1) / 2 * w.B * w.H_q
     # algorithmic backward work: the six gradient products (g = dO V^T, dV,
     # dQ, drho, and dK from q and from rho) plus recomputing s and r: 8
@@ -249,10 +369,11 @@ def bench_backward(w, steps, warmup, seed=None):
     return {"train_forward_us": t_fwd * 1e6, "backward_us": t_bwd * 1e6,
             "algorithmic_tflop": flops / 1e12, "tflops": flops / t_bwd / 1e12,
             "mfma_util": flops / t_bwd / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "launches": lst,
             "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
 
 
-def bench_projection(w, steps, warmup, d_model=None):
+def bench_projection(w, steps, warmup, d_model=None, flush=None):
     """Fused q, k, v, rho projection for the causal-prefill shapes: x
     [B, T, d_model] by the packed weight [(2 H_q + 2 H_kv) d, d_model]
     (d_model = H_q d unless given), bf16 in, bf16 out."""
@@ -268,7 +389,7 @@ def bench_projection(w, steps, warmup, d_model=None):
     wt = (torch.randn((N, C), generator=g, device=dev) * C ** -0.5).to(torch.bfloat16)
     kc = torch.zeros((w.B, w.H_kv, w.T, w.d), dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
-    run = lambda: pa.qkvr_projection(x, wt, w.H_q, w.H_kv, w.d, k_cache=kc, v_cache=vc)
+    run = lambda _i=0: pa.qkvr_projection(x, wt, w.H_q, w.H_kv, w.d, k_cache=kc, v_cache=vc)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -280,14 +401,16 @@ def bench_projection(w, steps, warmup, d_model=None):
     ev1.record()
     torch.cuda.synchronize()
     kern = ev0.elapsed_time(ev1) / steps / 1e3
+    lst = launch_stats(run, flush=flush)
     flops = 2.0 * w.B * w.T * N * C
     return {"kernel_us": kern * 1e6, "algorithmic_tflop": flops / 1e12,
             "tflops": flops / kern / 1e12,
             "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "launches": lst,
             "shape": dict(tokens=w.B * w.T, d_model=C, out_features=N)}
 
 
-def bench_chunked(w, steps, warmup, seed=None):
+def bench_chunked(w, steps, warmup, seed=None, flush=None):
     """Chunked prefill: w.T new rows after w.past cached tokens per sequence."""
     import torch
 
@@ -303,26 +426,33 @@ def bench_chunked(w, steps, warmup, seed=None):
             inp["v_cache"].data_ptr(), inp["past_lens"].data_ptr(), inp["chunk_lens"].data_ptr(),
             out.data_ptr(), w.B, w.H_q, w.H_kv, w.d, w.T, inp["k_cache"].shape[2],
             float(inp["scale"]), 0, stream)
-    for _ in range(warmup):
+
+    def one(_i=0):
         if L.parallax_prefill_chunked(*args) != 0:
             raise RuntimeError("chunked prefill failed")
+
+    for _ in range(warmup):
+        one()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(steps):
-        L.parallax_prefill_chunked(*args)
+        one()
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = ev0.elapsed_time(ev1) / steps / 1e3
+    lst = launch_stats(one, flush=flush)
     # row t sees past + t + 1 keys: 4 contractions of 2 d flops per (row, key)
     pairs = w.T * w.past + w.T * (w.T + 1) / 2
     flops = 8.0 * w.d * pairs * w.B * w.H_q
     return {"us_per_step": (t1 - t0) / steps * 1e6, "kernel_us": kern * 1e6,
             "algorithmic_tflop": flops / 1e12, "tflops": flops / kern / 1e12,
             "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "launches": lst,
+            "mfma_util_median": flops / (lst["median_us"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "shape": dict(B=w.B, T=w.T, past=w.past, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
 
 
@@ -343,7 +473,7 @@ def bench_tokens(T, steps, warmup, seed=None):
     caches = [(inp["k_cache"], inp["v_cache"])]
     for _ in range(7):
         caches.append((inp["k_cache"].clone(), inp["v_cache"].clone()))
-    ns, chunk = pa.decode_plan(w.B, w.H_q * T, w.H_kv, S_max, 0)
+    ns, chunk = pa.decode_plan(w.B, w.H_q * T, w.H_kv, w.d, S_max, 0)
     ws_bytes = max(pa.decode_workspace_size(w.B, w.H_q * T, w.d, ns), 16)
     ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device=dev)
     out = torch.empty((w.B, w.H_q, T, w.d), dtype=torch.float32, device=dev)
@@ -369,10 +499,11 @@ def bench_tokens(T, steps, warmup, seed=None):
     ev1.record()
     torch.cuda.synchronize()
     kern = ev0.elapsed_time(ev1) / steps / 1e3
+    lst = launch_stats(one)
     kv_bytes = w.B * w.H_kv * S_max * w.d * 2 * 2
     return {"kernel_us": kern * 1e6, "kv_bytes": kv_bytes, "GB_per_s": kv_bytes / kern / 1e9,
             "pct_of_hbm_peak": 100 * kv_bytes / kern / 1e9 / HBM_PEAK_GBS,
-            "num_splits": ns, "chunk": chunk,
+            "num_splits": ns, "chunk": chunk, "launches": lst,
             "shape": dict(B=w.B, H_q=w.H_q, H_kv=w.H_kv, d=w.d, new_tokens=T, cached=w.past)}
 
 
@@ -496,6 +627,42 @@ def cpu_baseline(runner, min_s=10.0, budget_s=30.0, prefill=None):
     return res
 
 
+def workload_registry(steps, warmup, flush, prefill_keep=None):
+    """name -> zero-argument function measuring that workload."""
+    from workloads import CHUNK_WORKLOAD, WORKLOADS, replace_shape
+
+    w2 = WORKLOADS[2]
+    w64 = replace_shape(w2, name="gqa-decode-d64", d=64, q_std=64 ** -0.25, k_std=64 ** -0.25)
+    w8 = replace_shape(w2, name="gqa8-decode", H_q=64)
+    reg = {
+        "gqa-decode-d64": lambda: bench_decode(
+            w64, 8, steps, max(3, warmup // 4), read_ref=True,
+            shape=dict(B=8, H_q=16, H_kv=8, d=64, kv_len=4096)),
+        "single-head-decode": lambda: bench_decode(
+            WORKLOADS[1], 1, max(10, steps // 2), max(3, warmup // 4), flush=flush),
+        "ragged-batch-decode": lambda: bench_decode(
+            WORKLOADS[3], 1, max(10, steps // 10), max(3, warmup // 4)),
+        "long-context-splitkv-decode": lambda: bench_decode(
+            WORKLOADS[4], 2, max(10, steps // 2), max(3, warmup // 4)),
+        "gqa8-decode": lambda: bench_decode(
+            w8, 8, steps, max(3, warmup // 4), shape=dict(B=8, H_q=64, H_kv=8, d=128, kv_len=4096)),
+    }
+    for T in (2, 3, 4):
+        reg[f"multi-token-decode-T{T}"] = (lambda T=T: bench_tokens(T, steps, max(3, warmup // 4)))
+    reg["causal-prefill"] = lambda: bench_prefill(WORKLOADS[5], max(5, steps // 20), 10,
+                                                  keep=prefill_keep, flush=flush)
+    reg["chunked-prefill"] = lambda: bench_chunked(CHUNK_WORKLOAD, max(5, steps // 10), 10,
+                                                   flush=flush)
+    reg["causal-prefill-backward"] = lambda: bench_backward(WORKLOADS[5], max(5, steps // 40), 5,
+                                                            flush=flush)
+    reg["qkvr-projection"] = lambda: bench_projection(WORKLOADS[5], max(5, steps // 10), 10,
+                                                      flush=flush)
+    return reg
+
+
+PREFILL_NAMES = ("causal-prefill", "chunked-prefill", "causal-prefill-backward", "qkvr-projection")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -505,6 +672,9 @@ def main():
                     help="all: every workload; main: the GQA decode line only; "
                          "prefill: the causal and chunked prefill, the prefill backward and "
                          "the q/k/v/rho projection only (for profiling)")
+    ap.add_argument("--only", default=None,
+                    help="measure this one workload alone and print {\"workloads\": {...}} "
+                         "(for profiling); gqa-decode is the main line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -517,7 +687,7 @@ def main():
 
     import torch
 
-    from workloads import CHUNK_WORKLOAD, WORKLOADS, replace_shape
+    from workloads import WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -532,15 +702,23 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    flush = Flusher()
+    prefill_keep = None if (args.no_cpu_baseline or args.only) else {}
+    reg = workload_registry(args.steps, args.warmup, flush, prefill_keep)
+
+    if args.only and args.only != WORKLOADS[2].name:
+        if args.only not in reg:
+            print(f"unknown workload {args.only}; choose from {sorted(reg)} or "
+                  f"{WORKLOADS[2].name}", file=sys.stderr)
+            sys.exit(2)
+        log(f"workload {args.only}")
+        print(json.dumps({"workloads": {args.only: reg[args.only]()}}), flush=True)
+        return
     if args.workloads == "prefill":
-        log("workload causal-prefill")
-        res = {WORKLOADS[5].name: bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10)}
-        log("workload chunked-prefill")
-        res[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
-        log("workload causal-prefill-backward")
-        res["causal-prefill-backward"] = bench_backward(WORKLOADS[5], max(5, args.steps // 40), 5)
-        log("workload qkvr-projection")
-        res["qkvr-projection"] = bench_projection(WORKLOADS[5], max(5, args.steps // 10), 10)
+        res = {}
+        for name in PREFILL_NAMES:
+            log(f"workload {name}")
+            res[name] = reg[name]()
         print(json.dumps({"workloads": res}), flush=True)
         return
 
@@ -582,6 +760,8 @@ def main():
         },
     }
     log(f"{w.name}: {gbs:.0f} GB/s per step, decode kernel {part_gbs:.0f} GB/s")
+    launches = main_r.launches()
+    result["launches"] = launches
     if all(n == w.S_max for n in main_r.lens):
         read_s = main_r.read_probe(args.steps, args.warmup)
         read_gbs = main_r.kv_bytes / read_s / 1e9
@@ -591,47 +771,18 @@ def main():
             "pct_of_hbm_peak": round(100 * read_gbs / HBM_PEAK_GBS, 2),
             "decode_over_read": round(part_gbs / read_gbs, 4)}
         log(f"plain read of the same bytes: {read_gbs:.0f} GB/s")
+    if args.only:
+        print(json.dumps({"workloads": {w.name: {
+            "kernel_us": part_s * 1e6, "launches": launches, "num_splits": main_r.ns}}}),
+            flush=True)
+        return
 
     workloads = {}
-    prefill_keep = None if args.no_cpu_baseline else {}
     if args.workloads == "all":
-        for idx, nbuf in ((1, 1), (3, 1), (4, 2)):
-            wi = WORKLOADS[idx]
-            log(f"workload {wi.name}")
-            r = DecodeRunner(wi, nbuf=nbuf)
-            ksteps = max(10, args.steps // (10 if idx == 3 else 2))
-            s, p = r.run(ksteps, max(3, args.warmup // 4))
-            workloads[wi.name] = {
-                "us_per_step": s * 1e6, "kernel_us": p * 1e6,
-                "kv_bytes": r.kv_bytes, "GB_per_s": r.kv_bytes / s / 1e9,
-                "pct_of_hbm_peak": 100 * r.kv_bytes / s / 1e9 / HBM_PEAK_GBS,
-                "num_splits": r.ns, "chunk": r.chunk, "steps": ksteps,
-                "dtype": "f32" if idx == 1 else "bf16"}
-            del r
+        for name, fn in reg.items():
+            log(f"workload {name}")
+            workloads[name] = fn()
             torch.cuda.empty_cache()
-        wg8 = replace_shape(WORKLOADS[2], name="gqa8-decode", H_q=64)
-        log(f"workload {wg8.name}")
-        r = DecodeRunner(wg8, nbuf=8)
-        s, p = r.run(args.steps, max(3, args.warmup // 4))
-        workloads[wg8.name] = {
-            "us_per_step": s * 1e6, "kernel_us": p * 1e6, "kv_bytes": r.kv_bytes,
-            "GB_per_s": r.kv_bytes / p / 1e9, "pct_of_hbm_peak": 100 * r.kv_bytes / p / 1e9 / HBM_PEAK_GBS,
-            "num_splits": r.ns, "chunk": r.chunk, "shape": dict(B=8, H_q=64, H_kv=8, d=128, kv_len=4096)}
-        del r
-        torch.cuda.empty_cache()
-        for T in (2, 3, 4):
-            log(f"workload multi-token-decode T={T}")
-            workloads[f"multi-token-decode-T{T}"] = bench_tokens(T, args.steps, max(3, args.warmup // 4))
-            torch.cuda.empty_cache()
-        log("workload causal-prefill")
-        workloads[WORKLOADS[5].name] = bench_prefill(WORKLOADS[5], max(5, args.steps // 20), 10,
-                                                     keep=prefill_keep)
-        log("workload chunked-prefill")
-        workloads[CHUNK_WORKLOAD.name] = bench_chunked(CHUNK_WORKLOAD, max(5, args.steps // 10), 10)
-        log("workload causal-prefill-backward")
-        workloads["causal-prefill-backward"] = bench_backward(WORKLOADS[5], max(5, args.steps // 40), 5)
-        log("workload qkvr-projection")
-        workloads["qkvr-projection"] = bench_projection(WORKLOADS[5], max(5, args.steps // 10), 10)
     result["workloads"] = workloads
 
     if not args.no_cpu_baseline:

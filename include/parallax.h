@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 6
+#define PARALLAX_ABI_VERSION 7
 
 typedef enum {
   PARALLAX_OK = 0,
@@ -82,18 +82,24 @@ int parallax_abi_version(void);
 const char* parallax_status_string(parallax_status_t s);
 
 /*
- * Split-KV plan for decode. Each (b, KV head, group of <= 4 query heads, or
- * <= 8 when the KV head serves more than 4) is
- * cut into `num_splits` contiguous key ranges of `chunk` keys (a multiple of
- * 128), processed by separate workgroups whose partial softmax states are
- * merged by the combine step. `requested` = 0 picks a plan from the device's
- * compute-unit count; a positive value asks for that many splits (rounded so
- * that chunk is a multiple of 128). Writes the plan to *num_splits and *chunk
- * (either may be NULL). Returns PARALLAX_ERR_BAD_SHAPE for sizes <= 0 or
- * H_q % H_kv != 0, PARALLAX_ERR_HIP if the device cannot be queried.
+ * Split-KV plan for decode (passage: the single pass over the KV stream of
+ * the blog "Parallax: Breaking the Boundary Bias with Parameterized Local
+ * Linear Attention", "Hardware Efficiency: Faster than Flash?"; the split
+ * and its merge are this library's). Each (b, KV head, group of <= 4 query
+ * heads, or <= 8 when the KV head serves more than 4) is cut into
+ * `num_splits` contiguous key ranges of `chunk` keys (a multiple of 128),
+ * processed by separate workgroups whose partial softmax states are merged
+ * by the combine step. `requested` = 0 picks a plan from the device's
+ * compute-unit count and the head dim d (about one workgroup per compute
+ * unit at d = 128, two at d = 64, whose rows are half as long); a positive
+ * value asks for that many splits (rounded so that chunk is a multiple of
+ * 128). Writes the plan to *num_splits and *chunk (either may be NULL).
+ * Returns PARALLAX_ERR_BAD_SHAPE for sizes <= 0 or H_q % H_kv != 0,
+ * PARALLAX_ERR_UNSUPPORTED for d not in {64, 128} or S_max > INT_MAX - 128,
+ * PARALLAX_ERR_HIP if the device cannot be queried.
  */
-parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int S_max, int requested,
-                                       int* num_splits, int* chunk);
+parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int d, int S_max,
+                                       int requested, int* num_splits, int* chunk);
 
 /*
  * Workspace bytes needed by parallax_decode / parallax_decode_partial for the
@@ -249,7 +255,7 @@ parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const
  *   dtype       PARALLAX_BF16 or PARALLAX_F32
  *   num_splits, workspace, workspace_bytes as parallax_decode, for
  *               H_q * T queries: the plan is parallax_decode_plan(B, H_q * T,
- *               H_kv, S_max, num_splits) and the size
+ *               H_kv, d, S_max, num_splits) and the size
  *               parallax_decode_workspace_size(B, H_q * T, d, num_splits);
  *               the same zeroed-counter rule applies.
  * Errors as parallax_decode (any number (H_q / H_kv) * T of (head, token)

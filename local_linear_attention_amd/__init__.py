@@ -93,7 +93,7 @@ def load_library(path: str) -> ctypes.CDLL:
     L.parallax_status_string.restype = ctypes.c_char_p
     L.parallax_status_string.argtypes = [i]
     L.parallax_decode_plan.restype = i
-    L.parallax_decode_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.parallax_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     L.parallax_decode_workspace_size.restype = sz
     L.parallax_decode_workspace_size.argtypes = [i, i, i, i]
     dec = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -179,10 +179,10 @@ def _stream_ptr(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def decode_plan(B: int, H_q: int, H_kv: int, S_max: int, num_splits: int = 0):
+def decode_plan(B: int, H_q: int, H_kv: int, d: int, S_max: int, num_splits: int = 0):
     """(num_splits, chunk) the library uses for these sizes (0 = automatic)."""
     ns, ch = ctypes.c_int(0), ctypes.c_int(0)
-    _check(lib().parallax_decode_plan(B, H_q, H_kv, S_max, num_splits, ctypes.byref(ns),
+    _check(lib().parallax_decode_plan(B, H_q, H_kv, d, S_max, num_splits, ctypes.byref(ns),
                                       ctypes.byref(ch)), "parallax_decode_plan")
     return ns.value, ch.value
 
@@ -212,7 +212,7 @@ def _decode_shapes(q, rho, k_cache, v_cache, seq_lens):
 
 
 def _workspace(B, H_q, H_kv, d, S_max, num_splits, workspace, device):
-    ns, _ = decode_plan(B, H_q, H_kv, S_max, num_splits)
+    ns, _ = decode_plan(B, H_q, H_kv, d, S_max, num_splits)
     need = decode_workspace_size(B, H_q, d, ns)
     if workspace is None:
         # zeroed: the fused merge's arrival counters must start at zero

@@ -42,10 +42,13 @@ constexpr int kChunkQuantum = 128;  // keys per workgroup pass (4 waves x 32 key
 constexpr int kMaxAutoSplits = 32;  // automatic plans use at most this many splits
 
 // Split plan: chunk (keys per workgroup, multiple of 128) and split count.
-parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* ns_out,
+parallax_status_t plan(int B, int H_q, int H_kv, int d, int S_max, int requested, int* ns_out,
                        int* chunk_out) {
-  if (B <= 0 || H_q <= 0 || H_kv <= 0 || S_max <= 0 || H_q % H_kv != 0)
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || S_max <= 0 || H_q % H_kv != 0)
     return PARALLAX_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
+  // the padded key range must stay an int
+  if (S_max > INT_MAX - kChunkQuantum) return PARALLAX_ERR_UNSUPPORTED;
   const int G = H_q / H_kv;
   const int hw = parallax::decode_heads_per_workgroup(G);
   const long long groups = (G + hw - 1) / hw;
@@ -66,7 +69,10 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
     // workgroup streams for so short a time that the merge's record reads
     // decide, while a few more splits still cut the latency of small batches
     // (one 1024-key sequence: 2 splits 11.0 us, 8 splits 7.5 us).
-    const long long target = (long long)cus;
+    // At d = 64 a workgroup's rows are half as long, so two workgroups per
+    // compute unit keep as many bytes in flight as one does at d = 128
+    // (gqa shape at d = 64: 4 splits 17.2 us, 8 splits 16.5 us).
+    const long long target = (long long)cus * (d <= 64 ? 2 : 1);
     long long want = ((long long)S_max * streams + target - 1) / target;
     if (want > 2048) want = 2048;  // the cap below, applied before the narrowing to int
     chunk = round_up(want, kChunkQuantum);
@@ -80,7 +86,7 @@ parallax_status_t plan(int B, int H_q, int H_kv, int S_max, int requested, int* 
     }
   }
   if (chunk > full) chunk = full;
-  const int ns = (S_max + chunk - 1) / chunk;
+  const int ns = (int)(((long long)S_max + chunk - 1) / chunk);
   if (ns_out) *ns_out = ns;
   if (chunk_out) *chunk_out = chunk;
   return PARALLAX_OK;
@@ -123,7 +129,7 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return PARALLAX_ERR_MISALIGNED;
   int ns = 0, chunk = 0;
-  parallax_status_t st = plan(B, H_q, H_kv, S_max, num_splits, &ns, &chunk);
+  parallax_status_t st = plan(B, H_q, H_kv, d, S_max, num_splits, &ns, &chunk);
   if (st != PARALLAX_OK) return st;
   if (ns > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid z
   const bool direct = (ns == 1);
@@ -202,11 +208,11 @@ const char* parallax_status_string(parallax_status_t s) {
   return "unknown parallax status";
 }
 
-parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int S_max, int requested,
+parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int d, int S_max, int requested,
                                        int* num_splits, int* chunk) {
   try {
     if (requested < 0) return PARALLAX_ERR_BAD_SHAPE;
-    return plan(B, H_q, H_kv, S_max, requested, num_splits, chunk);
+    return plan(B, H_q, H_kv, d, S_max, requested, num_splits, chunk);
   } catch (...) {
     return PARALLAX_ERR_HIP;
   }
@@ -246,7 +252,7 @@ parallax_status_t parallax_decode_combine(const int32_t* seq_lens, float* out, i
     if (d != 64 && d != 128) return PARALLAX_ERR_UNSUPPORTED;
     if (!aligned16(out)) return PARALLAX_ERR_MISALIGNED;
     int ns = 0, chunk = 0;
-    parallax_status_t st = plan(B, H_q, H_kv, S_max, num_splits, &ns, &chunk);
+    parallax_status_t st = plan(B, H_q, H_kv, d, S_max, num_splits, &ns, &chunk);
     if (st != PARALLAX_OK) return st;
     if (ns == 1) return PARALLAX_OK;
     const size_t need = workspace_bytes_for(B, H_q, d, ns);

@@ -53,6 +53,8 @@
 // The softmax max is rescaled lazily: only when a block's max exceeds the
 // running reference by more than 2^8, which keeps every exp below 256.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -111,78 +113,143 @@ __device__ __forceinline__ uint32_t load_probe_words(const T* p, int n, uint32_t
   return 0;
 }
 
-// Merges the partial records of splits 0..nsv-1 of one (b, h_q) at the two
-// dimensions 2 p and 2 p + 1 (records are REC = 2D+4 floats apart: m, l, Bs,
-// c, A[D], C[D]) and returns the two finalised outputs. Online over the
-// splits (the running max only grows; records with l = 0 hold no key and are
-// skipped; the probe reference is the first non-empty record's), with
-// the loads of 8 splits issued before any of them is used. kCoherent reads
-// with agent-scope atomic loads (records written by other workgroups in the
-// same launch, possibly through another XCD's L2).
-template <int D, bool kCoherent = false>
-__device__ __forceinline__ f32x2 merge_records(const float* __restrict__ base, int nsv, int p) {
-  constexpr int REC = 2 * D + 4;
-  constexpr int NB = 8;
-  auto get = [](const float* q) {
-    if constexpr (kCoherent)
-      return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Cache-policy operand of a buffer access that goes to the device-coherent
+// level (gfx950 "sc1"): records exchanged between the workgroups of one
+// launch, which may run on different XCDs, each with its own L2.
+constexpr int kCoherent = 16;
+
+// V consecutive floats (V = 1, 2, 4) as one value.
+template <int V> struct Vec;
+template <> struct Vec<1> { typedef float T; };
+template <> struct Vec<2> { typedef f32x2 T; };
+template <> struct Vec<4> { typedef f32x4 T; };
+
+// Record accesses at byte offset `off` of a workgroup's record range, which
+// starts at `base` and is also reached through the descriptor `r`. Four
+// floats move as one 16-byte buffer access (COH: at the device-coherent
+// level); one or two floats as global accesses (COH: agent-scope atomics,
+// also at the coherent level), which measured slightly faster than the
+// narrow buffer forms in the 4-head kernel.
+template <int V, bool COH>
+__device__ __forceinline__ typename Vec<V>::T rec_load(const float* base, __amdgpu_buffer_rsrc_t r,
+                                                       uint32_t off) {
+  if constexpr (V == 4) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, COH ? kCoherent : 0));
+  } else if constexpr (V == 2) {
+    const uint64_t* p = reinterpret_cast<const uint64_t*>(base + off / 4);
+    if constexpr (COH)
+      return __builtin_bit_cast(f32x2, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     else
-      return *q;
-  };
-  auto get2 = [](const float* q) {
-    if constexpr (kCoherent) {
-      const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(q), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      return __builtin_bit_cast(f32x2, u);
-    } else {
-      return *reinterpret_cast<const f32x2*>(q);
-    }
-  };
-  if (nsv <= 0) return f32x2{0.f, 0.f};
+      return __builtin_bit_cast(f32x2, *p);
+  } else {
+    const float* p = base + off / 4;
+    if constexpr (COH)
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      return *p;
+  }
+}
+
+template <int V, bool COH>
+__device__ __forceinline__ void rec_store(typename Vec<V>::T x, float* base, __amdgpu_buffer_rsrc_t r,
+                                          uint32_t off) {
+  if constexpr (V == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, COH ? kCoherent : 0);
+  } else if constexpr (V == 2) {
+    uint64_t* p = reinterpret_cast<uint64_t*>(base + off / 4);
+    if constexpr (COH)
+      __hip_atomic_store(p, __builtin_bit_cast(uint64_t, x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = __builtin_bit_cast(uint64_t, x);
+  } else {
+    float* p = base + off / 4;
+    if constexpr (COH)
+      __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = x;
+  }
+}
+
+// The 16-byte record header (m, l, Bs, c): one buffer access next to V = 4,
+// else four single floats, as the narrow forms above.
+template <int V, bool COH>
+__device__ __forceinline__ f32x4 hdr_load(const float* base, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (V == 4) {
+    return rec_load<4, COH>(base, r, off);
+  } else {
+    return f32x4{rec_load<1, COH>(base, r, off), rec_load<1, COH>(base, r, off + 4),
+                 rec_load<1, COH>(base, r, off + 8), rec_load<1, COH>(base, r, off + 12)};
+  }
+}
+
+template <int V, bool COH>
+__device__ __forceinline__ void hdr_store(f32x4 x, float* base, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (V == 4) {
+    rec_store<4, COH>(x, base, r, off);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rec_store<1, COH>(x[i], base, r, off + 4 * i);
+  }
+}
+
+// Merges the partial records of splits 0..nsv-1 of one (b, h_q) at the V
+// dimensions V q .. V q + V - 1 and returns the finalised outputs. Records
+// are REC = 2D+4 floats apart from byte offset `off0` of the descriptor `r`:
+// (m, l, Bs, c) as one 16-byte header, then A[D] and C[D]. Online over the
+// splits (the running max only grows; records with l = 0 hold no key and are
+// skipped; the probe reference is the first non-empty record's), with the
+// loads of 8 splits issued before any of them is used. COH reads at the
+// device-coherent level (records written in the same launch).
+template <int D, int V, bool COH>
+__device__ __forceinline__ typename Vec<V>::T merge_records(const float* base,
+                                                            __amdgpu_buffer_rsrc_t r, uint32_t off0,
+                                                            int nsv, int q) {
+  using VT = typename Vec<V>::T;
+  constexpr uint32_t RECB = (2 * D + 4) * 4;
+  constexpr int NB = 8;
+  if (nsv <= 0) return VT{};
   float c0 = 0.f;
   bool have = false;  // the reference c0 is the first non-empty record's
   float M = -INFINITY, l = 0.f, bs = 0.f;
-  f32x2 A = {0.f, 0.f}, C = {0.f, 0.f};
+  VT A{}, C{};
   for (int s0 = 0; s0 < nsv; s0 += NB) {
-    float ms[NB], lw[NB], bw[NB], cw[NB];
-    f32x2 Aw[NB], Cw[NB];
+    f32x4 hd[NB];
+    VT Aw[NB], Cw[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const float* rec = base + (size_t)min(s0 + i, nsv - 1) * REC;
-      ms[i] = get(rec + 0);
-      lw[i] = get(rec + 1);
-      bw[i] = get(rec + 2);
-      cw[i] = get(rec + 3);
-      Aw[i] = get2(rec + 4 + 2 * p);
-      Cw[i] = get2(rec + 4 + D + 2 * p);
+      const uint32_t rec = off0 + (uint32_t)min(s0 + i, nsv - 1) * RECB;
+      hd[i] = hdr_load<V, COH>(base, r, rec);
+      Aw[i] = rec_load<V, COH>(base, r, rec + 16 + 4 * V * q);
+      Cw[i] = rec_load<V, COH>(base, r, rec + 16 + 4 * D + 4 * V * q);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      if (s0 + i < nsv && lw[i] > 0.f) {  // a record with l = 0 holds no key
+      const float ms = hd[i][0], lw = hd[i][1], bw = hd[i][2], cw = hd[i][3];
+      if (s0 + i < nsv && lw > 0.f) {  // a record with l = 0 holds no key
         if (!have) {
-          c0 = cw[i];
+          c0 = cw;
           have = true;
         }
-        if (ms[i] > M) {
-          const float f = exp2f(M - ms[i]);
+        if (ms > M) {
+          const float f = exp2f(M - ms);
           l *= f;
           bs *= f;
           A *= f;
           C *= f;
-          M = ms[i];
+          M = ms;
         }
-        const float al = exp2f(ms[i] - M);
-        const float sh = cw[i] - c0;
-        l += al * lw[i];
-        bs += al * (bw[i] + sh * lw[i]);
+        const float al = exp2f(ms - M);
+        const float sh = cw - c0;
+        l += al * lw;
+        bs += al * (bw + sh * lw);
         A += al * Aw[i];
         C += al * (Cw[i] + sh * Aw[i]);
       }
     }
   }
-  if (!(l > 0.f)) return f32x2{0.f, 0.f};
-  const float g = 1.f + bs / l;
-  return (A * g - C) / l;
+  if (!(l > 0.f)) return VT{};
+  const float gn = 1.f + bs / l;
+  return (A * gn - C) / l;
 }
 
 // MT (several new tokens per sequence): every (query head, token) pair is a
@@ -202,7 +269,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   using P = Dec<T, D>;
   constexpr int HW = 4 * HG;                         // query heads per workgroup
   __shared__ __attribute__((aligned(16))) float lds_state[kWaves][HW][4];  // m, l, bs, cref per head
-  __shared__ float lds_vec[kWaves][2][HW][D];        // A, C per head
+  __shared__ __attribute__((aligned(16))) float lds_vec[kWaves][2][HW][D];  // A, C per head
   __shared__ __attribute__((aligned(16))) char k_lds[kWaves][P::KLDS];  // bf16: each wave's K block
 
   // Grid (KV head x head group, sequence, split): workgroups are dealt to
@@ -296,8 +363,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
 
   const size_t slice = ((size_t)b * H_kv + hk) * (size_t)S_max * D;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + slice, (uint32_t)n * P::ROWB);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + slice, (uint32_t)n * P::ROWB);
+  // The range ends at this workgroup's last key (j1 <= n): loads past it
+  // return zeros without touching memory.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + slice, (uint32_t)j1 * P::ROWB);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + slice, (uint32_t)j1 * P::ROWB);
 
   f32x4 acc[HG][P::DPL];
 #pragma unroll
@@ -338,10 +407,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
           vrs, (uint32_t)(blk + 16 * (e >> 2) + 4 * g + (e & 3)) * P::ROWB + P::DPL * c * P::ESZ);
   };
 
-  for (int blk = j0 + kBlockKeys * wave; blk < j1; blk += kBlockKeys * kWaves) {
-    Words<P::KW> kw[2][P::KSTEPS];
-    Words<P::VW> vw[8];
-    load_block(blk, kw, vw);
+  // Contracts block blk (its K and V pieces already in kw, vw).
+  auto process = [&](int blk, const Words<P::KW> (&kw)[2][P::KSTEPS], const Words<P::VW> (&vw)[8]) {
 
     // bf16: the block's K rows into this wave's LDS region (rows padded by
     // 16 bytes), then the A operand of each score MFMA (key row 16 T2 + c,
@@ -475,6 +542,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         }
       }
     }
+  };
+
+  for (int blk = j0 + kBlockKeys * wave; blk < j1; blk += kBlockKeys * kWaves) {
+    Words<P::KW> kw[2][P::KSTEPS];
+    Words<P::VW> vw[8];
+    load_block(blk, kw, vw);
+    process(blk, kw, vw);
   }
 
   // ---- per-wave state to LDS (a wave without blocks leaves l = 0)
@@ -500,70 +574,89 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   __syncthreads();
 
   // ---- merge the 4 waves; finalise (one split) or write the partial record.
-  // With the fused merge the records are written with agent-scope atomic
-  // stores, which go to the device-coherent level instead of staying in this
-  // XCD's L2, so the merging workgroup (on any XCD) reads them without any
-  // cache-wide write-back or invalidate.
-  auto put = [&](float* p, float v) {
-    if (fused)
-      __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      *p = v;
-  };
-  // Branch-free: every LDS read of the item is issued before any is used
-  // (the states of the 4 waves as one 16-byte read each), waves without keys
-  // (l = 0) get weight 0, and the reference c0 is the first wave's with keys.
-  for (int idx = tid; idx < Gw * D; idx += 256) {
-    const int h = idx / D;
-    const int dim = idx % D;
-    float4 st[kWaves];  // m, l, bs, cref
-    float Aw[kWaves], Cw[kWaves];
+  // The records of this workgroup's heads lie in one range of the workspace
+  // (heads h0 .. h0 + Gw - 1, every split), reached through one descriptor.
+  // With the fused merge they are written and read at the device-coherent
+  // level (kCoherent) instead of staying in this XCD's L2, so the merging
+  // workgroup (on any XCD) reads them without any cache-wide write-back or
+  // invalidate.
+  float* const wbase = direct ? out : ws + ((size_t)b * H_q + h0) * num_splits * P::REC;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(wbase, direct ? 0u : (uint32_t)(Gw * num_splits * P::REC * 4));
+  // V dimensions per thread, as many as keep all 256 threads busy (1, 2 or
+  // 4): wider LDS reads, record stores and record loads. Four only in the
+  // 8-head instantiation (4 x 128 dims never reach 1024 items), so that the
+  // 4-head kernel keeps its register count (164: three workgroups per
+  // compute unit in long, ragged batches).
+  const int V = (HG == 2 && Gw * D >= 1024) ? 4 : (Gw * D >= 512 ? 2 : 1);
+  // Waves merge in LDS. Branch-free: every LDS read of an item is issued
+  // before any is used (the states of the 4 waves as one 16-byte read each),
+  // waves without keys (l = 0) get weight 0, and the reference c0 is the
+  // first wave's with keys.
+  auto wave_merge = [&](auto vtag) {
+    constexpr int VV = decltype(vtag)::value;
+    using VT = typename Vec<VV>::T;
+    for (int idx = tid; idx < Gw * D / VV; idx += 256) {
+      const int h = idx / (D / VV);
+      const int q = idx % (D / VV);
+      float4 st[kWaves];  // m, l, bs, cref
+      VT Aw[kWaves], Cw[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      st[w] = *reinterpret_cast<const float4*>(&lds_state[w][h][0]);
-      Aw[w] = lds_vec[w][0][h][dim];
-      Cw[w] = lds_vec[w][1][h][dim];
-    }
-    float M = -INFINITY;
-    float c0 = 0.f;
-#pragma unroll
-    for (int w = kWaves - 1; w >= 0; --w) {
-      M = st[w].y > 0.f ? fmaxf(M, st[w].x) : M;
-      c0 = st[w].y > 0.f ? st[w].w : c0;
-    }
-    float l = 0.f, bs = 0.f, A = 0.f, C = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float lw = st[w].y;
-      const float al = lw > 0.f ? exp2f(st[w].x - M) : 0.f;
-      const float sh = st[w].w - c0;
-      l += al * lw;
-      bs += al * (st[w].z + sh * lw);
-      A += al * Aw[w];
-      C += al * (Cw[w] + sh * Aw[w]);
-    }
-    if (direct) {
-      out[((size_t)b * H_q + h0 + h) * D + dim] = l > 0.f ? (A * (1.f + bs / l) - C) / l : 0.f;
-    } else {
-      float* rec = ws + (((size_t)b * H_q + h0 + h) * num_splits + split) * P::REC;
-      if (dim == 0) {
-        put(rec + 0, M);
-        put(rec + 1, l);
-        put(rec + 2, bs);
-        put(rec + 3, c0);
+      for (int w = 0; w < kWaves; ++w) {
+        st[w] = *reinterpret_cast<const float4*>(&lds_state[w][h][0]);
+        Aw[w] = *reinterpret_cast<const VT*>(&lds_vec[w][0][h][VV * q]);
+        Cw[w] = *reinterpret_cast<const VT*>(&lds_vec[w][1][h][VV * q]);
       }
-      put(rec + 4 + dim, A);
-      put(rec + 4 + D + dim, C);
+      float M = -INFINITY;
+      float c0 = 0.f;
+#pragma unroll
+      for (int w = kWaves - 1; w >= 0; --w) {
+        M = st[w].y > 0.f ? fmaxf(M, st[w].x) : M;
+        c0 = st[w].y > 0.f ? st[w].w : c0;
+      }
+      float l = 0.f, bs = 0.f;
+      VT A{}, C{};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float lw = st[w].y;
+        const float al = lw > 0.f ? exp2f(st[w].x - M) : 0.f;
+        const float sh = st[w].w - c0;
+        l += al * lw;
+        bs += al * (st[w].z + sh * lw);
+        A += al * Aw[w];
+        C += al * (Cw[w] + sh * Aw[w]);
+      }
+      if (direct) {
+        *reinterpret_cast<VT*>(out + ((size_t)b * H_q + h0 + h) * D + VV * q) =
+            l > 0.f ? (A * (1.f + bs / l) - C) / l : VT{};
+      } else {
+        const uint32_t rec = (uint32_t)((h * num_splits + split) * P::REC * 4);
+        const f32x4 hd = {M, l, bs, c0};
+        if (fused) {
+          if (q == 0) hdr_store<VV, true>(hd, wbase, wrs, rec);
+          rec_store<VV, true>(A, wbase, wrs, rec + 16 + 4 * VV * q);
+          rec_store<VV, true>(C, wbase, wrs, rec + 16 + 4 * D + 4 * VV * q);
+        } else {
+          if (q == 0) hdr_store<VV, false>(hd, wbase, wrs, rec);
+          rec_store<VV, false>(A, wbase, wrs, rec + 16 + 4 * VV * q);
+          rec_store<VV, false>(C, wbase, wrs, rec + 16 + 4 * D + 4 * VV * q);
+        }
+      }
     }
-  }
+  };
+  if (HG == 2 && V == 4)
+    wave_merge(std::integral_constant<int, 4 * HG / 2>{});
+  else if (V == 2)
+    wave_merge(std::integral_constant<int, 2>{});
+  else
+    wave_merge(std::integral_constant<int, 1>{});
   if (direct || !fused) return;
 
   // ---- fused merge: the workgroup that finishes last for this (b, KV head,
   // head group) merges every split's record. Each thread waits until its own
   // coherent record stores have completed before the workgroup barrier, so
   // they are performed before thread 0's arrival increment; the last arrival
-  // reads the records with agent-scope atomic loads (also at the coherent
-  // level) and returns the counter to zero.
+  // reads the records at the coherent level and returns the counter to zero.
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -576,24 +669,27 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
   __syncthreads();
   if (!s_last) return;
-  // The merging workgroup acquires at agent scope before it reads the other
-  // workgroups' records: stale lines of this XCD's caches are invalidated.
-  // Only this one workgroup per stream pays for it.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int nsv = (n + chunk - 1) / chunk;
-  for (int idx = tid; idx < Gw * D / 2; idx += 256) {  // (head, pair of dims)
-    const int h = idx / (D / 2);
-    const int p = idx % (D / 2);
-    const float* base = ws + ((size_t)b * H_q + h0 + h) * num_splits * P::REC;
-    *reinterpret_cast<f32x2*>(out + ((size_t)b * H_q + h0 + h) * D + 2 * p) =
-        merge_records<D, true>(base, nsv, p);
-  }
+  auto split_merge = [&](auto vtag) {
+    constexpr int VV = decltype(vtag)::value;
+    using VT = typename Vec<VV>::T;
+    for (int idx = tid; idx < Gw * D / VV; idx += 256) {  // (head, VV dims)
+      const int h = idx / (D / VV);
+      const int q = idx % (D / VV);
+      *reinterpret_cast<VT*>(out + ((size_t)b * H_q + h0 + h) * D + VV * q) =
+          merge_records<D, VV, true>(wbase, wrs, (uint32_t)(h * num_splits * P::REC * 4), nsv, q);
+    }
+  };
+  if (HG == 2 && V == 4)
+    split_merge(std::integral_constant<int, 4 * HG / 2>{});
+  else  // pairs at least (the single-float form measured slower)
+    split_merge(std::integral_constant<int, 2>{});
 }
 
-// One workgroup of D/2 threads per (b, h_q): merges the partial records of
+// One workgroup of D/4 threads per (b, h_q): merges the partial records of
 // the splits that hold keys and writes out[b, h_q, :].
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const int32_t* __restrict__ seq_lens,
+__global__ __launch_bounds__(32) void decode_combine_kernel(const int32_t* __restrict__ seq_lens,
                                                              const float* __restrict__ ws,
                                                              float* __restrict__ out, int H_q,
                                                              int S_max, int chunk, int num_splits) {
@@ -602,8 +698,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const int32_t* __res
   const int b = bh / H_q;
   const int n = min(max(seq_lens[b], 0), S_max);
   const int nsv = min(num_splits, (n + chunk - 1) / chunk);
-  *reinterpret_cast<f32x2*>(out + (size_t)bh * D + 2 * threadIdx.x) =
-      merge_records<D>(ws + (size_t)bh * num_splits * REC, nsv, threadIdx.x);
+  const float* base = ws + (size_t)bh * num_splits * REC;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)(num_splits * REC * 4));
+  *reinterpret_cast<f32x4*>(out + (size_t)bh * D + 4 * threadIdx.x) =
+      merge_records<D, 4, false>(base, r, 0u, nsv, threadIdx.x);
 }
 
 template <typename T, int D, bool MT, int HG>
@@ -641,11 +739,11 @@ hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.B * a.H_q);
   if (a.d == 64) {
-    hipLaunchKernelGGL((decode_combine_kernel<64>), grid, dim3(32), 0, st, a.seq_lens,
+    hipLaunchKernelGGL((decode_combine_kernel<64>), grid, dim3(16), 0, st, a.seq_lens,
                        static_cast<const float*>(a.ws), a.out, a.H_q, a.S_max, a.chunk,
                        a.num_splits);
   } else {
-    hipLaunchKernelGGL((decode_combine_kernel<128>), grid, dim3(64), 0, st, a.seq_lens,
+    hipLaunchKernelGGL((decode_combine_kernel<128>), grid, dim3(32), 0, st, a.seq_lens,
                        static_cast<const float*>(a.ws), a.out, a.H_q, a.S_max, a.chunk,
                        a.num_splits);
   }

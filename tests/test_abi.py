@@ -70,9 +70,9 @@ def test_status_strings(L):
     assert "unknown" in pa.status_string(99)
 
 
-def _plan(L, B, Hq, Hkv, S, req):
+def _plan(L, B, Hq, Hkv, S, req, d=128):
     ns, ch = ctypes.c_int(-1), ctypes.c_int(-1)
-    st = L.parallax_decode_plan(B, Hq, Hkv, S, req, ctypes.byref(ns), ctypes.byref(ch))
+    st = L.parallax_decode_plan(B, Hq, Hkv, d, S, req, ctypes.byref(ns), ctypes.byref(ch))
     return st, ns.value, ch.value
 
 
@@ -89,6 +89,22 @@ def test_plan_requested(L):
 def test_plan_bad_shapes(L):
     for args in [(0, 1, 1, 10, 1), (1, 3, 2, 10, 1), (1, 2, 2, 0, 1), (1, 2, 2, 10, -1)]:
         assert _plan(L, *args)[0] == SHAPE
+    assert _plan(L, 1, 2, 2, 10, 1, d=0)[0] == SHAPE
+    assert _plan(L, 1, 2, 2, 10, 1, d=96)[0] == UNSUP
+
+
+def test_plan_largest_key_range(L):
+    """Key ranges whose padding to a multiple of 128 would not fit an int are
+    refused instead of producing a plan with no splits."""
+    import ctypes as ct
+
+    int_max = 2 ** 31 - 1
+    for req in (1, 3):
+        st, ns, ch = _plan(L, 1, 1, 1, int_max, req)
+        assert st == UNSUP
+        st, ns, ch = _plan(L, 1, 1, 1, int_max - 128, req)
+        assert st == OK and ns >= 1 and ch > 0 and ch % 128 == 0
+        assert ns * ch >= int_max - 128
 
 
 def test_workspace_size(L):
@@ -230,7 +246,7 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         pa.lib()
     with pytest.raises(RuntimeError, match="missing"):
-        pa.decode_plan(1, 2, 1, 128, 2)
+        pa.decode_plan(1, 2, 1, 64, 128, 2)
 
 
 @fake_pointers

@@ -19,7 +19,7 @@ def test_decode_graph_replays_match_eager():
               for s in range(4)]
     st = {k: v.clone() for k, v in inputs[0].items() if isinstance(v, torch.Tensor)}
     scale = inputs[0]["scale"]
-    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.S_max, 4)
+    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.d, w.S_max, 4)
     ws = torch.zeros(pa.decode_workspace_size(w.B, w.H_q, w.d, ns) // 4, dtype=torch.float32,
                      device="cuda")
     out = torch.empty((w.B, w.H_q, w.d), dtype=torch.float32, device="cuda")

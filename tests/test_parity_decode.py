@@ -160,7 +160,7 @@ def test_deterministic_bitwise_static_paths():
     w = SMALL2
     dev = to_dev(make_decode_inputs(w, seq_lens=[700, 333, 97]))
     assert np.array_equal(run_decode(dev, 1), run_decode(dev, 1))
-    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.S_max, 4)
+    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.d, w.S_max, 4)
     ws = torch.empty(pa.decode_workspace_size(w.B, w.H_q, w.d, ns) // 4, device="cuda")
     outs = []
     for _ in range(2):
@@ -181,7 +181,7 @@ def test_fused_deterministic_bitwise():
 def test_two_phase_equals_one_shot():
     w = SMALL2
     dev = to_dev(make_decode_inputs(w, seq_lens=[700, 333, 97]))
-    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.S_max, 4)
+    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.d, w.S_max, 4)
     ws = torch.empty(pa.decode_workspace_size(w.B, w.H_q, w.d, ns) // 4, device="cuda")
     out = torch.empty(w.B, w.H_q, w.d, device="cuda")
     pa.decode_partial(dev["q"], dev["rho"], dev["k_cache"], dev["v_cache"], dev["seq_lens"],
@@ -256,7 +256,7 @@ def test_workload4_full_sampled():
 def test_fused_workspace_reuse_counters_return_to_zero():
     """One zeroed workspace serves successive fused calls with different lengths."""
     w = SMALL2
-    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.S_max, 6)
+    ns, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.d, w.S_max, 6)
     nbytes = pa.decode_workspace_size(w.B, w.H_q, w.d, ns)
     ws = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
     rec_words = w.B * w.H_q * ns * (2 * w.d + 4)

@@ -117,7 +117,7 @@ def test_matches_chunked_prefill():
 
 def test_workspace_reuse_counts_return_to_zero():
     w = small(T=2)
-    ns, _ = pa.decode_plan(w.B, w.H_q * w.T, w.H_kv, 720, 5)
+    ns, _ = pa.decode_plan(w.B, w.H_q * w.T, w.H_kv, w.d, 720, 5)
     ws = torch.zeros(pa.decode_workspace_size(w.B, w.H_q * w.T, w.d, ns) // 4, device="cuda")
     rec_words = w.B * w.H_q * w.T * ns * (2 * w.d + 4)
     for past, clen in (([700, 33, 256], [2, 1, 2]), ([0, 718, 5], [2, 2, 0]), ([10, 10, 10], [0, 0, 0])):
