@@ -85,6 +85,26 @@ __device__ __forceinline__ i32x4 bf16x8_to_f16x8(i32x4 x) {
   return r;
 }
 
+// Sum and max of x over the lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four
+// lane groups that hold one query row), with the CDNA4 lane swaps
+// (v_permlane16_swap / v_permlane32_swap: VALU, no LDS round trip). Each swap
+// of x with itself leaves x_l and x_{l^16} (x_{l^32}) in the two results, in
+// an order that depends on the lane, so every lane of a row gets the same
+// (commutative) sum.
+__device__ __forceinline__ float row_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 constexpr int kRows = 128;      // query rows per workgroup
 constexpr int kWaves = 8;       // 16 rows per wave
 constexpr int kThreads = 64 * kWaves;
@@ -269,8 +289,7 @@ __device__ __forceinline__ void prefill_rows(
     // Lazy rescale: each lane checks its own 8 keys; the row max (two
     // exchanges) is formed only when some lane exceeds the bound.
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2)) {
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = row_max4(mx);
       const bool need = mx > m + kRescaleLog2;
       const float mnew = need ? mx : m;
       const float alpha = need ? exp2f(m - mnew) : 1.0f;
@@ -408,8 +427,7 @@ __device__ __forceinline__ void prefill_rows(
     //    exact: Bs -> Bs - delta l and C -> C - delta A.
     const bool moved = __builtin_amdgcn_ballot_w64(mx > m + kRefLog2) != 0;
     if (moved) {
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = row_max4(mx);
       const bool need = mx > m + kRescaleLog2;
       const float mnew = need ? mx : m;
       const float alpha = need ? exp2f(m - mnew) : 1.0f;
@@ -451,10 +469,8 @@ __device__ __forceinline__ void prefill_rows(
         ltot += ev[e];
         btot += ev[e] * rc[e >> 2][e & 3];
       }
-      ltot += __shfl_xor(ltot, 16);
-      ltot += __shfl_xor(ltot, 32);
-      btot += __shfl_xor(btot, 16);
-      btot += __shfl_xor(btot, 32);
+      ltot = row_sum4(ltot);
+      btot = row_sum4(btot);
       const float delta = btot / ltot;  // key 0 is visible to every row: ltot > 0
       bsum -= delta * lsum;
       rinit -= delta;
@@ -526,10 +542,8 @@ __device__ __forceinline__ void prefill_rows(
   }
 
   // ---- finalise: row totals of l and Bs, moved to the output layout
-  float ltot = lsum + __shfl_xor(lsum, 16);
-  ltot += __shfl_xor(ltot, 32);
-  float btot = bsum + __shfl_xor(bsum, 16);
-  btot += __shfl_xor(btot, 32);
+  const float ltot = row_sum4(lsum);
+  const float btot = row_sum4(bsum);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int lr = 4 * g + i;  // row within the wave held by this lane's accumulators
