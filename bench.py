@@ -98,16 +98,16 @@ def read_traffic(workload: str, prefix: str = "decode_partial"):
     return vals
 
 
-def traffic_entry(workload: str, algorithmic_bytes: float, prefix: str = "decode_partial"):
+def traffic_entry(workload: str, algorithmic_read_bytes: float, prefix: str = "decode_partial"):
     """The `traffic` fields of a workload entry (None when not measured on
-    these sources)."""
+    these sources); reads are compared with the algorithmic read bytes."""
     t = read_traffic(workload, prefix)
     if t is None:
         return {"traffic": None}
     tot = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
     return {"traffic": int(tot), "traffic_fetch_bytes": int(t["fetch_bytes_per_launch"]),
             "traffic_write_bytes": int(t["write_bytes_per_launch"]),
-            "fetch_over_algorithmic": round(t["fetch_bytes_per_launch"] / algorithmic_bytes, 4)}
+            "fetch_over_algorithmic": round(t["fetch_bytes_per_launch"] / algorithmic_read_bytes, 4)}
 
 
 class Flusher:
@@ -313,16 +313,16 @@ def bench_prefill(w, steps, warmup, seed=None, keep=None, flush=None):
     # algorithmic work: q.k, rho.k, e.v and (e r).v over the causal half, 2 d flops each
     flops = 8.0 * w.d * (w.T * (w.T + 1) / 2) * w.B * w.H_q
     # algorithmic bytes: q, rho, K, V read once (bf16), out written once (fp32)
-    io = (2 * w.B * w.H_q * w.T * w.d + 2 * w.B * w.H_kv * w.T * w.d) * 2 \
-        + w.B * w.H_q * w.T * w.d * 4
+    reads = (2 * w.B * w.H_q * w.T * w.d + 2 * w.B * w.H_kv * w.T * w.d) * 2
+    writes = w.B * w.H_q * w.T * w.d * 4
     res = {"us_per_step": (t1 - t0) / steps * 1e6, "kernel_us": kern * 1e6,
            "algorithmic_tflop": flops / 1e12, "tflops": flops / kern / 1e12,
            "mfma_util": flops / kern / 1e12 / MFMA_BF16_PEAK_TFLOPS,
            "launches": lst,
            "mfma_util_median": flops / (lst["median_us"] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-           "algorithmic_io_bytes": io,
+           "algorithmic_read_bytes": reads, "algorithmic_write_bytes": writes,
            "shape": dict(B=w.B, T=w.T, H_q=w.H_q, H_kv=w.H_kv, d=w.d)}
-    res.update(traffic_entry(w.name, io, prefix="prefill"))
+    res.update(traffic_entry(w.name, reads, prefix="prefill"))
     return res
 
 
@@ -773,8 +773,8 @@ def main():
         log(f"plain read of the same bytes: {read_gbs:.0f} GB/s")
     if args.only:
         print(json.dumps({"workloads": {w.name: {
-            "kernel_us": part_s * 1e6, "launches": launches, "num_splits": main_r.ns}}}),
-            flush=True)
+            "kernel_us": part_s * 1e6, "launches": launches, "num_splits": main_r.ns,
+            "kv_bytes": main_r.kv_bytes}}}), flush=True)
         return
 
     workloads = {}
