@@ -426,32 +426,16 @@ __device__ __forceinline__ void prefill_rows(
     //    stay small next to the weights that dominate the row. The shift is
     //    exact: Bs -> Bs - delta l and C -> C - delta A.
     const bool moved = __builtin_amdgcn_ballot_w64(mx > m + kRefLog2) != 0;
-    if (moved) {
+    float alpha = 1.0f;
+    if (moved) {  // VALU only: the row max through lane swaps
       mx = row_max4(mx);
       const bool need = mx > m + kRescaleLog2;
       const float mnew = need ? mx : m;
-      const float alpha = need ? exp2f(m - mnew) : 1.0f;
+      alpha = need ? exp2f(m - mnew) : 1.0f;
       m = mnew;
       lsum *= alpha;
       bsum *= alpha;
-      // accumulator rows 4 g + i belong to the lanes whose column is 4 g + i
-      float arow[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int j = 0; j < P::DPL; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          accA[j][i] *= arow[i];
-          accC[j][i] *= arow[i];
-        }
     }
-
-    // ---- weights e and e (r - c), each rounded once to fp16 (toward zero):
-    // the A operands of the value MFMAs. l and Bs sum the rounded values, so
-    // the weights that reach A and C are exactly those of l and Bs, and the
-    // rounding only perturbs each weight by 2^-11 of itself instead of
-    // leaving A out of step with l.
     float ev[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ev[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 2][e & 3], sl, -m));
@@ -463,27 +447,43 @@ __device__ __forceinline__ void prefill_rows(
       }
     }
     if (moved) {
-      float ltot = lsum, btot = bsum;
+      // One pass over the accumulators for both moves, with one broadcast
+      // round trip: A <- alpha A and C <- alpha (C - delta A).
+      float le = 0.f, be = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        ltot += ev[e];
-        btot += ev[e] * rc[e >> 2][e & 3];
+        le += ev[e];
+        be += ev[e] * rc[e >> 2][e & 3];
       }
-      ltot = row_sum4(ltot);
-      btot = row_sum4(btot);
-      const float delta = btot / ltot;  // key 0 is visible to every row: ltot > 0
+      const float ltot = row_sum4(lsum + le);
+      const float btot = row_sum4(bsum + be);
+      // any reference is exact; key 0 is visible to every row, so ltot > 0
+      const float delta = btot * __builtin_amdgcn_rcpf(ltot);
       bsum -= delta * lsum;
       rinit -= delta;
 #pragma unroll
       for (int T2 = 0; T2 < 2; ++T2) rc[T2] -= delta;
-      float drow[4];
+      // accumulator rows 4 g + i belong to the lanes whose column is 4 g + i
+      float arow[4], drow[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) drow[i] = __shfl(delta, 4 * g + i);
+      for (int i = 0; i < 4; ++i) {
+        arow[i] = __shfl(alpha, 4 * g + i);
+        drow[i] = __shfl(delta, 4 * g + i);
+      }
 #pragma unroll
       for (int j = 0; j < P::DPL; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) accC[j][i] = __builtin_fmaf(-drow[i], accA[j][i], accC[j][i]);
+        for (int i = 0; i < 4; ++i) {
+          accC[j][i] = __builtin_fmaf(-drow[i], accA[j][i], accC[j][i]) * arow[i];
+          accA[j][i] *= arow[i];
+        }
     }
+
+    // ---- weights e and e (r - c), each rounded once to fp16 (toward zero):
+    // the A operands of the value MFMAs. l and Bs sum the rounded values, so
+    // the weights that reach A and C are exactly those of l and Bs, and the
+    // rounding only perturbs each weight by 2^-11 of itself instead of
+    // leaving A out of step with l.
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     uint32_t pw[4], fw[4];
 #pragma unroll
