@@ -37,6 +37,15 @@
 // a heavy (late) and a light (early) row block, so every workgroup carries
 // the same causal work.
 //
+// Short chunks (at most 64 rows, e.g. a few new tokens after a long cache)
+// would leave most of the chip idle with 128-row blocks. They take 16-row
+// (up to 32 rows) or 32-row blocks, one per workgroup, and split each row
+// block's keys into 4 contiguous ranges: a step stages the next block of
+// every range, each of the first 4 TL waves (TL tiles of 16 rows per range)
+// contracts its own range's block, the remaining waves only help stage, and
+// at the end the ranges' (m, l, Bs, c, A, C) merge in LDS into the range-0
+// waves. Each step's loads are issued two steps ahead.
+//
 // Weights of the value contraction. Inference (prefill, chunked prefill):
 // e and e (r - c) are rounded once to fp16 and V is staged as fp16 (exact for
 // bf16 values of magnitude 2^-14 .. 65504), two products per value tile.
@@ -105,13 +114,16 @@ __device__ __forceinline__ float row_max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-constexpr int kRows = 128;      // query rows per workgroup
 constexpr int kWaves = 8;       // 16 rows per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeys = 32;       // keys per block
 constexpr int kNB = 2;          // key blocks per barrier
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kRefLog2 = 3.0f;       // block-max jump that moves the probe reference
+
+// Key blocks staged per barrier: kNB consecutive blocks with one key range
+// per workgroup (NS = 1), else one block of each of the NS key ranges.
+constexpr int slots_for(int NS) { return NS == 1 ? kNB : NS; }
 
 template <int D>
 struct Pre {
@@ -128,38 +140,49 @@ struct Pre {
   static constexpr int TILE = kKeys * VSTR;           // bytes of one staged K or V tile
 };
 
-// One row block (128 query rows starting at rb * 128) of one (b, h). TRAIN
+// One row block (16 TL query rows starting at rb 16 TL) of one (b, h). With
+// NS > 1 (short chunks) the first NS TL waves are NS key ranges times TL
+// tiles of 16 rows: each streams one range of the keys its rows see, and the
+// ranges' partial states merge in LDS at the end; any further waves only
+// help stage the key blocks. TRAIN
 // (the training forward, which also writes mu_v and the row statistics the
 // backward recomputes the weights from) contracts the weights as split bf16
 // pairs against bf16 V; otherwise they are rounded once to fp16 against fp16 V.
-template <int D, bool TRAIN>
+template <int D, bool TRAIN, int NS, int TL>
 __device__ __forceinline__ void prefill_rows(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ past_lens, float* __restrict__ out, float* __restrict__ mu_out,
     float4* __restrict__ stats, int H_q, int H_kv, int G, int T, int S_max, float scale_log2, int rb,
-    int h, int b, char (&kv_lds)[2 * kNB][2][Pre<D>::TILE]) {
+    int h, int b, char (&kv_lds)[2 * slots_for(NS)][2][Pre<D>::TILE]) {
   using P = Pre<D>;
+  static_assert(NS == 1 || !TRAIN, "key ranges are split in the inference form only");
+  static_assert(NS * TL <= kWaves && (NS > 1 || TL == kWaves), "wave roles");
+  constexpr int SLOTS = slots_for(NS);
+  constexpr int TILES = TL;          // 16-row tiles
+  constexpr int ROWS = 16 * TILES;   // query rows of the workgroup
   const int hk = h / G;
   // Row t of this chunk sits at position past + t of the sequence and sees
   // keys 0 .. past + t of the cache; rows t >= n are zero.
   const int past = past_lens ? min(max(past_lens[b], 0), S_max) : 0;
   const int n = min(min(max(seq_lens[b], 0), T), S_max - past);
-  const int R0 = rb * kRows;
+  const int R0 = rb * ROWS;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int rt = wave % TILES;  // this wave's row tile
+  const int sp = wave / TILES;  // this wave's key range (NS and up: staging only)
   const int lane = tid & 63;
   const int g = lane >> 4;     // lane group
   const int c = lane & 15;     // query row within the wave (score layout) / output column
-  const int wrow0 = R0 + 16 * wave;
+  const int wrow0 = R0 + 16 * rt;
   const int my_row = wrow0 + c;
 
   const size_t qbase = ((size_t)b * H_q + h) * (size_t)T * D;
   float* obase = out + qbase;
 
   if (R0 >= n) {  // whole block past the sequence: zeros
-    for (int i = tid; i < kRows * D / 4; i += kThreads) {
+    for (int i = tid; i < ROWS * D / 4; i += kThreads) {
       const int r = R0 + i / (D / 4);
       if (r < T) {
         reinterpret_cast<float4*>(obase + (size_t)r * D)[i % (D / 4)] = float4{0.f, 0.f, 0.f, 0.f};
@@ -168,7 +191,7 @@ __device__ __forceinline__ void prefill_rows(
       }
     }
     if (stats)
-      for (int r = R0 + tid; r < min(R0 + kRows, T); r += kThreads)
+      for (int r = R0 + tid; r < min(R0 + ROWS, T); r += kThreads)
         stats[((size_t)b * H_q + h) * T + r] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
@@ -204,9 +227,11 @@ __device__ __forceinline__ void prefill_rows(
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + kvslice, (uint32_t)(past + n) * P::ROWB);
 
   // keys this workgroup needs, and this wave's number of key blocks
-  const int wg_keys = past + min(R0 + kRows, n);
+  const int wg_keys = past + min(R0 + ROWS, n);
   const int nkb = (wg_keys + kKeys - 1) / kKeys;
   const int wave_nkb = wrow0 < n ? (past + min(wrow0 + 15, n - 1)) / kKeys + 1 : 0;
+  // key ranges: blocks [i spl, (i + 1) spl) form range i
+  const int spl = (nkb + NS - 1) / NS;
   const int my_pos = past + my_row;  // last key this lane's row sees
 
   // Tile pieces of this thread (16 bytes each). With PPT >= 2 the first half
@@ -222,7 +247,10 @@ __device__ __forceinline__ void prefill_rows(
       idx = tid % (kThreads / 2);
     }
   };
-  i32x4 stage[kNB][P::PPT];
+  // register stages: one (NS = 1), or two with split key ranges, whose
+  // steps contract only one block per wave and so cover less load latency
+  constexpr int NREG = NS == 1 ? 1 : 2;
+  i32x4 stage[NREG][SLOTS][P::PPT];
   auto load_tile = [&](int kb, i32x4 (&dst)[P::PPT]) {
 #pragma unroll
     for (int i = 0; i < P::PPT; ++i) {
@@ -457,8 +485,9 @@ __device__ __forceinline__ void prefill_rows(
       }
       const float ltot = row_sum4(lsum + le);
       const float btot = row_sum4(bsum + be);
-      // any reference is exact; key 0 is visible to every row, so ltot > 0
-      const float delta = btot * __builtin_amdgcn_rcpf(ltot);
+      // Any reference is exact. A row with no visible key yet (in a key range
+      // after the first, the rows before its first key) keeps its reference.
+      const float delta = ltot > 0.f ? btot * __builtin_amdgcn_rcpf(ltot) : 0.f;
       bsum -= delta * lsum;
       rinit -= delta;
 #pragma unroll
@@ -509,41 +538,150 @@ __device__ __forceinline__ void prefill_rows(
     }
   };
 
-  // Pipeline, one barrier per kNB blocks of keys: blocks kb .. kb + kNB - 1
-  // are contracted from LDS buffers pb .. pb + kNB - 1 while the next kNB
-  // blocks go from registers into the other buffers and the kNB blocks after
-  // them are loaded from HBM into the registers just freed (each load has kNB
-  // blocks of contraction to land). Two blocks per barrier halve the barriers
+  // Pipeline, one barrier per step of SLOTS staged blocks: the blocks of
+  // step s are contracted from LDS buffers pb .. pb + SLOTS - 1 while the
+  // next step's blocks go from registers into the other buffers and the step
+  // after them is loaded from HBM into the registers just freed (each load
+  // has a step of contraction to land). With one key range (NS = 1) a step
+  // holds kNB consecutive blocks: two blocks per barrier halve the barriers
   // and the LDS operand waits that follow each one (causal prefill about 2%
   // faster than one block per barrier; three or four blocks gave no more).
-  // Loads and stores run unconditionally: loads past the sequence are
-  // range-checked to zeros without touching memory. The loop is unrolled by
-  // two groups so that every buffer index is static.
-  auto groupstep = [&](int kb, int pb) {
+  // With NS ranges a step holds the s-th block of each range, and each wave
+  // contracts its own range's. Loads and stores run unconditionally: loads
+  // past the sequence are range-checked to zeros without touching memory.
+  // The loop is unrolled by two steps so that every buffer index is static.
+  auto block_of = [&](int st, int i) { return NS == 1 ? st * SLOTS + i : i * spl + st; };
+  const int nsteps = NS == 1 ? (nkb + SLOTS - 1) / SLOTS : spl;
+  // Step st: contract the blocks of step st from LDS buffers pb ..; move the
+  // register stage holding step st + 1 into the other buffers; refill that
+  // stage with step st + 1 + NREG.
+  auto step = [&](int st, int pb, i32x4 (&rs)[SLOTS][P::PPT]) {
+    if constexpr (NS == 1) {
 #pragma unroll
-    for (int i = 0; i < kNB; ++i)
-      if (kb + i < wave_nkb) contract(kb + i, pb + i);
+      for (int i = 0; i < SLOTS; ++i)
+        if (block_of(st, i) < wave_nkb) contract(block_of(st, i), pb + i);
+    } else {  // one contraction, from this wave's range's buffer (wave-uniform)
+      const int kb = block_of(st, sp);
+      if (sp < NS && kb < wave_nkb && st < spl) contract(kb, pb + sp);
+    }
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) store_tile((pb ^ kNB) + i, stage[i]);
+    for (int i = 0; i < SLOTS; ++i) store_tile((pb ^ SLOTS) + i, rs[i]);
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) load_tile(kb + 2 * kNB + i, stage[i]);
+    for (int i = 0; i < SLOTS; ++i) load_tile(block_of(st + 1 + NREG, i), rs[i]);
     __syncthreads();
   };
 #pragma unroll
-  for (int i = 0; i < kNB; ++i) load_tile(i, stage[i]);
+  for (int i = 0; i < SLOTS; ++i) load_tile(block_of(0, i), stage[0][i]);
 #pragma unroll
-  for (int i = 0; i < kNB; ++i) store_tile(i, stage[i]);
+  for (int i = 0; i < SLOTS; ++i) store_tile(i, stage[0][i]);
 #pragma unroll
-  for (int i = 0; i < kNB; ++i) load_tile(kNB + i, stage[i]);
+  for (int r = 0; r < NREG; ++r)
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) load_tile(block_of(1 + r, i), stage[(1 + r) % NREG][i]);
   __syncthreads();
-  for (int kb = 0; kb < nkb; kb += 2 * kNB) {
-    groupstep(kb, 0);
-    if (kb + kNB < nkb) groupstep(kb + kNB, kNB);
+  // Both steps of an iteration are unconditional and an odd last step runs
+  // after the loop: the loop is then entered only with the stages in one age
+  // order, so the load waits count just the loads a store needs.
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, 0, stage[1 % NREG]);
+    step(st + 1, SLOTS, stage[0]);
   }
+  if (st < nsteps) step(st, 0, stage[1 % NREG]);
 
   // ---- finalise: row totals of l and Bs, moved to the output layout
-  const float ltot = row_sum4(lsum);
-  const float btot = row_sum4(bsum);
+  float ltot = row_sum4(lsum);
+  float btot = row_sum4(bsum);
+  if constexpr (NS > 1) {
+    // Merge the key ranges of each row tile into the wave of range 0. Each
+    // range's state: per row (score layout) m, l, Bs and the reference c;
+    // per lane the accumulators (output layout). A range without keys has
+    // l = 0 and weight 0; the reference becomes range 0's (key 0 is in it).
+    float* f = reinterpret_cast<float*>(&kv_lds[0][0][0]);
+    float* rstat = f;                               // [NS][TILES][16 rows][4]
+    float* rvec = f + NS * TILES * 16 * 4;          // [NS - 1][TILES][64 lanes][2 DPL 4]
+    constexpr int VW = 2 * P::DPL * 4;
+    if (g == 0 && sp < NS) {
+      float* st4 = rstat + ((sp * TILES + rt) * 16 + c) * 4;
+      st4[0] = m;
+      st4[1] = ltot;
+      st4[2] = btot;
+      st4[3] = -rinit[0];
+    }
+    if (sp > 0 && sp < NS) {
+      float* v = rvec + (((sp - 1) * TILES + rt) * 64 + lane) * VW;
+#pragma unroll
+      for (int j = 0; j < P::DPL; ++j) {
+        *reinterpret_cast<f32x4*>(v + 8 * j) = accA[j];
+        *reinterpret_cast<f32x4*>(v + 8 * j + 4) = accC[j];
+      }
+    }
+    __syncthreads();
+    if (sp > 0) return;
+    // per-row weights of every range, in both layouts: row c (scalars) and
+    // rows 4 g + i (accumulators)
+    auto row_weights = [&](int r, float& M, float& c0) {
+      M = -INFINITY;
+      c0 = rstat[((0 * TILES + rt) * 16 + r) * 4 + 3];
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const float* st4 = rstat + ((s2 * TILES + rt) * 16 + r) * 4;
+        M = st4[1] > 0.f ? fmaxf(M, st4[0]) : M;
+      }
+    };
+    {
+      float M, c0;
+      row_weights(c, M, c0);
+      float l = 0.f, bs = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const float* st4 = rstat + ((s2 * TILES + rt) * 16 + c) * 4;
+        const float al = st4[1] > 0.f ? exp2f(st4[0] - M) : 0.f;
+        l += al * st4[1];
+        bs += al * (st4[2] + (st4[3] - c0) * st4[1]);
+      }
+      ltot = l;
+      btot = bs;
+      m = M;  // the training statistics are not kept with several ranges
+    }
+    // accumulators (rows 4 g + i): this wave's own range first, then one
+    // range at a time (a rolled loop, so that only one range's values are
+    // held in registers at once)
+    float M4[4], c04[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      row_weights(4 * g + i, M4[i], c04[i]);
+      const float* st4 = rstat + ((0 * TILES + rt) * 16 + 4 * g + i) * 4;
+      const float al = st4[1] > 0.f ? exp2f(st4[0] - M4[i]) : 0.f;
+      const float sh = st4[3] - c04[i];
+#pragma unroll
+      for (int j = 0; j < P::DPL; ++j) {
+        accC[j][i] = al * (accC[j][i] + sh * accA[j][i]);
+        accA[j][i] = al * accA[j][i];
+      }
+    }
+#pragma unroll 1
+    for (int s2 = 1; s2 < NS; ++s2) {
+      float al[4], sh[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* st4 = rstat + ((s2 * TILES + rt) * 16 + 4 * g + i) * 4;
+        al[i] = st4[1] > 0.f ? exp2f(st4[0] - M4[i]) : 0.f;
+        sh[i] = st4[3] - c04[i];
+      }
+      const float* v = rvec + (((s2 - 1) * TILES + rt) * 64 + lane) * VW;
+#pragma unroll
+      for (int j = 0; j < P::DPL; ++j) {
+        const f32x4 aw = *reinterpret_cast<const f32x4*>(v + 8 * j);
+        const f32x4 cw = *reinterpret_cast<const f32x4*>(v + 8 * j + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accA[j][i] += al[i] * aw[i];
+          accC[j][i] += al[i] * (cw[i] + sh[i] * aw[i]);
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int lr = 4 * g + i;  // row within the wave held by this lane's accumulators
@@ -575,18 +713,21 @@ __device__ __forceinline__ void prefill_rows(
   }
 }
 
-// Workgroup x handles row blocks nrb - 1 - x and x of one (b, h): under the
-// causal mask their key counts add up to the same total for every x, so all
-// workgroups carry equal work and the short early row blocks never form a
-// tail of their own.
-template <int D, bool TRAIN>
+// With one key range (NS = 1), workgroup x handles row blocks nrb - 1 - x
+// and x of one (b, h): under the causal mask their key counts add up to the
+// same total for every x, so all workgroups carry equal work and the short
+// early row blocks never form a tail of their own. Short chunks (NS > 1),
+// whose row blocks all see about the same keys, take one row block per
+// workgroup, so that a few rows per head still fill the chip.
+template <int D, bool TRAIN, int NS, int TL>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ past_lens, float* __restrict__ out, float* __restrict__ mu_out,
     float4* __restrict__ stats, int H_q, int H_kv, int G, int T, int S_max, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) char kv_lds[2 * kNB][2][Pre<D>::TILE];  // [buffer][K, V]
-  const int nrb = (T + kRows - 1) / kRows;
+  // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) char kv_lds[2 * slots_for(NS)][2][Pre<D>::TILE];
+  const int nrb = (T + 16 * TL - 1) / (16 * TL);
   // Workgroups are dealt to the 8 XCDs in linear order. Remap so that each
   // XCD takes a contiguous range of (sequence, head, row-block pair) tiles:
   // the query heads of one KV head are adjacent, so the workgroups running at
@@ -601,20 +742,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     h = (int)((L / npairs) % gridDim.y);
     b = (int)(L / (npairs * gridDim.y));
   }
-  prefill_rows<D, TRAIN>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
-                  scale_log2, nrb - 1 - x, h, b, kv_lds);
-  if (x != nrb - 1 - x) {
-    __syncthreads();
-    prefill_rows<D, TRAIN>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q, H_kv, G, T, S_max,
-                    scale_log2, x, h, b, kv_lds);
+  if constexpr (NS > 1) {
+    prefill_rows<D, TRAIN, NS, TL>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q,
+                                   H_kv, G, T, S_max, scale_log2, x, h, b, kv_lds);
+  } else {
+    prefill_rows<D, TRAIN, NS, TL>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q,
+                                   H_kv, G, T, S_max, scale_log2, nrb - 1 - x, h, b, kv_lds);
+    if (x != nrb - 1 - x) {
+      __syncthreads();
+      prefill_rows<D, TRAIN, NS, TL>(q, rho, kc, vc, seq_lens, past_lens, out, mu_out, stats, H_q,
+                                     H_kv, G, T, S_max, scale_log2, x, h, b, kv_lds);
+    }
   }
 }
 
-template <int D, bool TRAIN>
+template <int D, bool TRAIN, int NS, int TL>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  const int nrb = (a.T + kRows - 1) / kRows;
-  dim3 grid((nrb + 1) / 2, a.H_q, a.B);  // row blocks paired heavy + light
-  hipLaunchKernelGGL((prefill_kernel<D, TRAIN>), grid, dim3(kThreads), 0, st,
+  const int nrb = (a.T + 16 * TL - 1) / (16 * TL);
+  // one row block per workgroup with split key ranges, else pairs (heavy + light)
+  dim3 grid(NS > 1 ? nrb : (nrb + 1) / 2, a.H_q, a.B);
+  hipLaunchKernelGGL((prefill_kernel<D, TRAIN, NS, TL>), grid, dim3(kThreads), 0, st,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.rho),
                      static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v), a.seq_lens,
                      a.past_lens, a.out, a.mu_out, static_cast<float4*>(a.stats), a.H_q, a.H_kv,
@@ -622,13 +769,23 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Inference forms by chunk length: up to 32 rows, four key ranges of one
+// 16-row tile (half the waves contract, all of them stage keys); up to 64,
+// four ranges of two tiles; longer chunks, one range of eight tiles.
+template <int D>
+hipError_t launch_prefill_infer(const PrefillArgs& a, hipStream_t st) {
+  if (a.T <= 32) return launch_prefill_t<D, false, 4, 1>(a, st);
+  if (a.T <= 64) return launch_prefill_t<D, false, 4, 2>(a, st);
+  return launch_prefill_t<D, false, 1, kWaves>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
-  const bool train = a.mu_out != nullptr;
-  if (a.d == 64)
-    return train ? launch_prefill_t<64, true>(a, st) : launch_prefill_t<64, false>(a, st);
-  return train ? launch_prefill_t<128, true>(a, st) : launch_prefill_t<128, false>(a, st);
+  if (a.mu_out != nullptr)  // training forward
+    return a.d == 64 ? launch_prefill_t<64, true, 1, kWaves>(a, st)
+                     : launch_prefill_t<128, true, 1, kWaves>(a, st);
+  return a.d == 64 ? launch_prefill_infer<64>(a, st) : launch_prefill_infer<128>(a, st);
 }
 
 }  // namespace parallax

@@ -102,6 +102,27 @@ def test_multi_token_decode(T):
     check(replace_shape(SMALL, T=T, past=2000))
 
 
+@pytest.mark.parametrize("T", [1, 16, 17, 32, 33, 48, 64, 65, 127])
+def test_short_chunks(T):
+    """Chunks of up to 64 rows split the keys of each row block into 4 ranges
+    and merge the ranges' states (16-row blocks up to 32 rows, 32-row blocks
+    up to 64); 65 and 127 rows take the one-range path."""
+    check(replace_shape(SMALL, T=T, past=2000))
+
+
+@pytest.mark.parametrize("T", [9, 32, 50])
+def test_short_chunks_d64(T):
+    w = replace_shape(SMALL, T=T, past=1500, d=64, q_std=64 ** -0.25, k_std=64 ** -0.25)
+    check(w)
+
+
+def test_short_chunks_ragged():
+    """Split key ranges with chunk lengths and pasts that differ per sequence
+    (one empty chunk, one whose keys fit in the first range)."""
+    w = replace_shape(SMALL, B=4, T=48)
+    check(w, past_lens=[1900, 0, 37, 700], chunk_lens=[48, 17, 0, 31], S_max=2000)
+
+
 def test_ragged_past_and_chunk_lengths():
     w = replace_shape(SMALL, B=3)
     check(w, past_lens=[300, 0, 41], chunk_lens=[160, 77, 0], S_max=500)
