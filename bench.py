@@ -661,7 +661,7 @@ def workload_registry(steps, warmup, flush, prefill_keep=None):
             wc, max(10, steps // 2), 10, flush=flush))
     reg["causal-prefill-backward"] = lambda: bench_backward(WORKLOADS[5], max(5, steps // 40), 5,
                                                             flush=flush)
-    reg["qkvr-projection"] = lambda: bench_projection(WORKLOADS[5], max(5, steps // 10), 10,
+    reg["qkvr-projection"] = lambda: bench_projection(WORKLOADS[5], max(20, steps // 4), 10,
                                                       flush=flush)
     return reg
 

@@ -135,6 +135,22 @@ size_t parallax_decode_workspace_size(int B, int H_q, int d, int num_splits);
  * followed by parallax_decode_combine, up to rounding). With several splits
  * the workspace's counters must be zero on entry (see
  * parallax_decode_workspace_size); they are zero again on exit.
+ * Passage: the output equation of the blog "Parallax: Breaking the Boundary
+ * Bias with Parameterized Local Linear Attention", "The Core Insight:
+ * Covariance Correction" (out = mu_v - S_KV rho), with rho the per-token
+ * learned probe of the paper page "Parallax: Parameterized Local Linear
+ * Attention for Language Modeling", "Abstract", computed in the single pass
+ * over the KV stream of the blog's "Hardware Efficiency: Faster than Flash?"
+ * (streaming form: out = (A (1 + Bs / l) - C) / l over l = sum w, A = sum w v,
+ * Bs = sum w r, C = sum w r v, r = rho . k, softmax weights w).
+ * Errors: PARALLAX_ERR_NULL_POINTER (q, rho, a cache, seq_lens or out NULL);
+ * PARALLAX_ERR_BAD_SHAPE (a size <= 0, H_q % H_kv != 0, num_splits < 0, scale
+ * not finite); PARALLAX_ERR_UNSUPPORTED (d not in {64, 128}, dtype not bf16
+ * or fp32, B > 65535, a (b, h_kv) slice of 2 GiB or more, more than 65535
+ * splits); PARALLAX_ERR_MISALIGNED (a tensor or the workspace not 16-byte
+ * aligned, seq_lens not 4-byte aligned); PARALLAX_ERR_WORKSPACE (workspace
+ * NULL or smaller than parallax_decode_workspace_size for the plan);
+ * PARALLAX_ERR_HIP (device query or launch failed).
  */
 parallax_status_t parallax_decode(const void* q, const void* rho, const void* k_cache,
                                   const void* v_cache, const int32_t* seq_lens, float* out,
@@ -179,7 +195,12 @@ parallax_status_t parallax_decode_noalloc(const void* q, const void* rho, const 
  * First phase of decode: streams every valid K/V row once and writes one
  * partial state per (b, h_q, split) to `workspace` (or, when the resolved
  * plan has one split, finalises straight into `out`, which may otherwise be
- * NULL). Arguments as parallax_decode. Does not use the workspace counters.
+ * NULL). Arguments, passage and errors as parallax_decode (out may be NULL
+ * unless the plan has one split). Does not use the workspace counters.
+ * Record of (b, h_q, split) (fp32, 2 d + 4 values): running max m of the
+ * scaled scores (log2 units), l, Bs and the probe reference c of the
+ * streaming form (Bs and C relative to c), then A and C, each a d-vector
+ * relative to the weights 2^(s - m).
  */
 parallax_status_t parallax_decode_partial(const void* q, const void* rho, const void* k_cache,
                                           const void* v_cache, const int32_t* seq_lens,
@@ -193,7 +214,15 @@ parallax_status_t parallax_decode_partial(const void* q, const void* rho, const 
  * parallax_decode_partial with the same (B, H_q, H_kv, d, S_max, num_splits)
  * and writes out [B, H_q, d] fp32. Splits that start at or past seq_lens[b]
  * are skipped (never read). A no-op returning PARALLAX_OK when the resolved
- * plan has one split.
+ * plan has one split. Passage as parallax_decode: the merge rescales each
+ * record to the common max and moves it to the common probe reference
+ * (Bs -> Bs + (c_s - c) l_s, C -> C + (c_s - c) A_s, exact) before the
+ * streaming form's final step.
+ * Errors: PARALLAX_ERR_NULL_POINTER (seq_lens or out NULL);
+ * PARALLAX_ERR_BAD_SHAPE and PARALLAX_ERR_UNSUPPORTED as parallax_decode for
+ * the sizes and d; PARALLAX_ERR_MISALIGNED (out or the workspace not 16-byte
+ * aligned); PARALLAX_ERR_WORKSPACE (workspace NULL or too small);
+ * PARALLAX_ERR_HIP.
  */
 parallax_status_t parallax_decode_combine(const int32_t* seq_lens, float* out, int B, int H_q,
                                           int H_kv, int d, int S_max, int num_splits,
@@ -207,6 +236,26 @@ parallax_status_t parallax_decode_combine(const int32_t* seq_lens, float* out, i
  *   seq_lens  [B]                  int32 (device); rows t >= seq_lens[b] -> 0
  *   out       [B, H_q, T, d]       fp32, written in full
  * Needs no workspace. Only dtype PARALLAX_BF16 is built for prefill.
+ * Passage: the output equation of the blog "Parallax: Breaking the Boundary
+ * Bias with Parameterized Local Linear Attention", "The Core Insight:
+ * Covariance Correction", for every query row of a causal sequence, with the
+ * per-token probe of the paper page "Parallax: Parameterized Local Linear
+ * Attention for Language Modeling", "Abstract" (the pages' pretraining
+ * setting), computed per row in the streaming form given for
+ * parallax_decode.
+ * Precision: the softmax weights w and the products w (r - c) enter the
+ * value contraction rounded once to fp16 (toward zero, with l and Bs summed
+ * from the same rounded values) and V is staged as fp16, exact for bf16
+ * values of magnitude 2^-14 .. 65504; smaller magnitudes lose low bits (fp16
+ * subnormals) and larger ones are not representable. Measured per-row error
+ * against an fp64 evaluation: a few 1e-4 at unit-scale inputs, up to about
+ * 1.3e-3 with probes 20 times stronger and a sharp softmax.
+ * Errors: PARALLAX_ERR_NULL_POINTER (any pointer NULL); PARALLAX_ERR_BAD_SHAPE
+ * (a size <= 0, H_q % H_kv != 0, T > S_max, scale not finite);
+ * PARALLAX_ERR_UNSUPPORTED (dtype not bf16, d not in {64, 128}, B or H_q
+ * above 65535, a (b, h_kv) slice or a (b, h_q) block of 2 GiB or more);
+ * PARALLAX_ERR_MISALIGNED (a tensor not 16-byte aligned, seq_lens not 4-byte
+ * aligned); PARALLAX_ERR_HIP (launch failed).
  */
 parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k,
                                    const void* v, const int32_t* seq_lens, float* out, int B,
@@ -228,8 +277,13 @@ parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k
  *                                    clamped to [0, min(T, S_max - past)];
  *                                    rows t >= chunk_lens[b] are written as 0
  *   out         [B, H_q, T, d]       fp32, written in full
- * Only dtype PARALLAX_BF16 is built. Errors as parallax_prefill, plus
- * PARALLAX_ERR_NULL_POINTER for a NULL past_lens.
+ * Only dtype PARALLAX_BF16 is built. Passage and precision as
+ * parallax_prefill, with the chunk's rows placed after the cached tokens
+ * (the causal reading of continuing a sequence). Chunks of at most 64 rows
+ * split each row block's keys into 4 ranges whose partial states are merged
+ * exactly (rescaled to a common max and moved to a common probe reference).
+ * Errors as parallax_prefill, plus PARALLAX_ERR_NULL_POINTER for a NULL
+ * past_lens and PARALLAX_ERR_MISALIGNED for a past_lens not 4-byte aligned.
  */
 parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const void* k_cache,
                                            const void* v_cache, const int32_t* past_lens,

@@ -12,17 +12,23 @@
 //   [q | k | v | rho] = x W^T,  W = [W_Q; W_K; W_V; W_R]  ((2 H_q + 2 H_kv) d rows, d_model cols)
 //   q, rho -> [B, H_q, T, d];  k, v -> rows past_b + t of the cache [B, H_kv, S_max, d]
 //
-// Tiling. A workgroup of 8 waves computes 256 output features x 256 tokens;
-// each wave 128 features x 64 tokens as 8 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16 with the features as the MFMA rows (128
-// accumulator registers; two waves per SIMD). The larger wave tile halves
-// the LDS operand reads per MFMA against 64 x 64 wave tiles. K (d_model)
-// advances 64 at a time through double-buffered LDS (rows padded by 16 bytes
-// so the 16-row operand reads hit distinct banks), with two register stages
-// so each global load has two stages of contraction to land. Within a k-step
-// the operand reads of half the feature tiles are issued before their MFMAs
-// (order pinned by scheduling barriers). Loads past x's or W's rows come back
-// as zeros (range-checked buffer loads).
+// Tiling. A workgroup of 4 waves computes 256 output features x 256 tokens;
+// each wave 128 features x 128 tokens as 8 x 8 tiles of
+// v_mfma_f32_16x16x32_bf16 with the features as the MFMA rows: 256
+// accumulator registers, held in the accumulation registers at one wave per
+// SIMD. The operand bytes a wave reads from LDS grow with its tile's rows
+// plus columns while its MFMA work grows with their product, so the square
+// 128 x 128 wave tile reads a third fewer LDS bytes per MFMA than two waves
+// of 128 x 64 per SIMD (whose operand reads and staging writes kept the LDS
+// as busy as the matrix pipe). K (d_model) advances 64 at a time through
+// double-buffered LDS (chunks XOR-swizzled per row against bank conflicts).
+// With one wave per SIMD nothing else hides a wave's
+// LDS and global latency, so the wave pipelines its own: between the rows
+// of one k-step's MFMAs it reads the next k-step's operands, stores the next
+// stage from registers into the other buffer and loads the stage after it,
+// and the next stage's first operands are read under the current stage's
+// last MFMAs (one barrier per stage, between its two k-steps). Loads past
+// x's or W's rows come back as zeros (range-checked buffer loads).
 //
 // Epilogue. Each wave writes its tile to LDS token-major, then every token's
 // 128 features (consecutive dims of one or two heads) leave as 16-byte stores,
@@ -36,31 +42,48 @@ namespace parallax {
 namespace {
 
 constexpr int kWF = 128;                 // features per wave
-constexpr int kWX = 64;                  // tokens per wave
+constexpr int kWX = 128;                 // tokens per wave
 constexpr int kNWF = 2;                  // waves along features
-constexpr int kNWX = 4;                  // waves along tokens
+constexpr int kNWX = 2;                  // waves along tokens
 constexpr int kThreads = 64 * kNWF * kNWX;
 constexpr int kTileF = kWF * kNWF;       // 256 features per workgroup
 constexpr int kTileX = kWX * kNWX;       // 256 tokens per workgroup
 constexpr int kK = 64;                   // d_model per stage
-constexpr int kStr = kK * 2 + 16;        // LDS row stride (bytes)
+constexpr int kStr = kK * 2;             // LDS row stride (bytes, unpadded)
+// Byte offset of 16-byte chunk ch (0..7) of staged row r: the chunks of each
+// row are permuted by an XOR with (r & 7) ^ ((r >> 3) & 1), so the operand
+// reads (16 consecutive rows, one chunk) and the staging writes (whole rows)
+// both spread over distinct banks.
+__device__ __forceinline__ int swz(int r, int ch) { return (ch ^ ((r & 7) ^ ((r >> 3) & 1))) * 16; }
 constexpr int kFI = kWF / 16;            // MFMA tiles per wave along features
 constexpr int kXJ = kWX / 16;            // MFMA tiles per wave along tokens
 constexpr int kPPW = kTileF * kK * 2 / 16 / kThreads;  // W pieces (16 bytes) per thread per stage
 constexpr int kPPX = kTileX * kK * 2 / 16 / kThreads;  // x pieces per thread per stage
 constexpr int kBuf = (kTileF + kTileX) * kStr;         // one LDS buffer: W tile then x tile
 constexpr int kEStr = kWF * 2 + 16;      // epilogue: bytes per token row (16-byte aligned)
-static_assert(kNWF * kNWX * kWX * kEStr <= 2 * kBuf, "epilogue tiles must fit in the stage buffers");
+// LDS: the two stage buffers, reused by the epilogue's token-major tiles
+constexpr int kLds = 2 * kBuf > kNWF * kNWX * kWX * kEStr ? 2 * kBuf : kNWF * kNWX * kWX * kEStr;
 
-__global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
+// acc += a b (v_mfma_f32_16x16x32_bf16) with the accumulator bound to the
+// accumulation registers. Left to itself the register allocator splits the
+// 256 accumulator registers between the two register files and moves them
+// every stage. Each accumulator is next used 64 MFMAs later (no dependency
+// stall); the epilogue waits explicitly before reading them.
+__device__ __forceinline__ void mfma_agpr(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// One workgroup per CU (its 4 waves, one per SIMD, may use the whole
+// register file).
+__global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int c = lane & 15;
   const int wf = wave / kNWX;  // feature half of the tile
-  const int wx = wave % kNWX;  // token quarter of the tile
+  const int wx = wave % kNWX;  // token half of the tile
   // Tile order. Workgroups are dealt to the 8 XCDs in linear order: remap so
   // each XCD takes a contiguous range, and walk that range in groups of 8 x 8
   // (token, feature) tiles, so the workgroups an XCD runs at once share 8
@@ -94,34 +117,23 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
 
   // Thread tid's pieces: rows (tid + kThreads i) / 8, 16-byte column
   // (tid + kThreads i) % 8 of the stage. Past d_model the offsets run into
-  // the next row (in range, unused) or past the last row (zeros).
-  // The stage offset kt * 128 bytes goes in the scalar offset operand.
-  auto load = [&](int kt, i32x4 (&sw)[kPPW], i32x4 (&sx)[kPPX]) {
-    const int soff = __builtin_amdgcn_readfirstlane(kt * kK * 2);
-#pragma unroll
-    for (int i = 0; i < kPPW; ++i) {
-      const int idx = tid + kThreads * i;
-      sw[i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (uint32_t)(idx / 8) * KB + (idx % 8) * 16, soff, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kPPX; ++i) {
-      const int idx = tid + kThreads * i;
-      sx[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (uint32_t)(idx / 8) * KB + (idx % 8) * 16, soff, 0);
-    }
+  // the next row (in range, unused) or past the last row (zeros). One
+  // per-lane offset serves every piece: the row step 32 i and the stage
+  // offset go in the scalar offset operand.
+  const uint32_t voff = (uint32_t)(tid / 8) * KB + (tid % 8) * 16;
+  const uint32_t loff = (uint32_t)(tid / 8) * kStr + swz(tid / 8, tid % 8);
+  i32x4 sw[kPPW], sx[kPPX];
+  auto load_piece = [&](int kt, int i) {
+    const int soff = __builtin_amdgcn_readfirstlane(kt * kK * 2 + i * (kThreads / 8) * KB);
+    sw[i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, voff, soff, 0);
+    sx[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, voff, soff, 0);
   };
-  auto store = [&](int buf, const i32x4 (&sw)[kPPW], const i32x4 (&sx)[kPPX]) {
-    char* base = lds + buf * kBuf;
-#pragma unroll
-    for (int i = 0; i < kPPW; ++i) {
-      const int idx = tid + kThreads * i;
-      *reinterpret_cast<i32x4*>(base + (idx / 8) * kStr + (idx % 8) * 16) = sw[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kPPX; ++i) {
-      const int idx = tid + kThreads * i;
-      *reinterpret_cast<i32x4*>(base + (kTileF + idx / 8) * kStr + (idx % 8) * 16) = sx[i];
-    }
+  auto store_piece = [&](int buf, int i) {
+    char* base = lds + buf * kBuf + loff + i * (kThreads / 8) * kStr;
+    *reinterpret_cast<i32x4*>(base) = sw[i];
+    *reinterpret_cast<i32x4*>(base + kTileF * kStr) = sx[i];
   };
+  static_assert(kPPW == kPPX && kPPW == kFI, "one W and one x piece per feature row of MFMAs");
 
   f32x4 acc[kFI][kXJ];
 #pragma unroll
@@ -129,64 +141,80 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int j = 0; j < kXJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One stage from LDS buffer buf. A operand of feature tile t in lane
-  // (g, c): feature row 16 t + c, d_model 32 ks + 8 g .. + 7; B operand of
-  // token tile t likewise with token rows.
-  auto compute = [&](int buf) {
-    const char* wb = lds + buf * kBuf + (kWF * wf + c) * kStr + 16 * g;
-    const char* xb = lds + buf * kBuf + (kTileF + kWX * wx + c) * kStr + 16 * g;
+  // A operand of feature tile t in lane (g, c): feature row 16 t + c,
+  // d_model 32 ks + 8 g .. + 7 of the stage; B operand of token tile t
+  // likewise with token rows.
+  auto rd_a = [&](int buf, int ks, int t) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(
+        lds + buf * kBuf + (kWF * wf + 16 * t + c) * kStr + swz(c, g + 4 * ks)));
+  };
+  auto rd_b = [&](int buf, int ks, int t) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(
+        lds + buf * kBuf + (kTileF + kWX * wx + 16 * t + c) * kStr + swz(c, g + 4 * ks)));
+  };
+  auto mfma_rows = [&](int i0, int i1, const bf16x8 (&af)[kFI], const bf16x8 (&bx)[kXJ]) {
 #pragma unroll
-    for (int ks = 0; ks < kK / 32; ++ks) {
-      bf16x8 bx[kXJ];
+    for (int i = i0; i < i1; ++i)
 #pragma unroll
-      for (int t = 0; t < kXJ; ++t)
-        bx[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(xb + 16 * t * kStr + 64 * ks));
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 af[kFI / 2];
-#pragma unroll
-        for (int t = 0; t < kFI / 2; ++t)
-          af[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(
-                      wb + 16 * (t + hf * kFI / 2) * kStr + 64 * ks));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < kFI / 2; ++i)
-#pragma unroll
-          for (int j = 0; j < kXJ; ++j)
-            acc[i + hf * kFI / 2][j] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bx[j], acc[i + hf * kFI / 2][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+      for (int j = 0; j < kXJ; ++j) mfma_agpr(acc[i][j], af[i], bx[j]);
   };
 
-  // Stage kt is contracted from buffer kt % 2 while stage kt + 1 goes from
-  // registers into the other buffer and stage kt + 3 is loaded into the
-  // registers just freed. The loop is unrolled by two so that the register
-  // stage of each step is static; stores and loads past the last stage move
-  // zeros or unused data and are never contracted.
-  i32x4 sw[2][kPPW], sx[2][kPPX];
+  // Software pipeline, one barrier per stage. On entry to stage kt the
+  // first k-step's operands (a0, b0) are in registers. Each feature row of
+  // its MFMAs is followed by two reads of the second k-step's operands, the
+  // store of one staged W piece and one x piece (stage kt + 1) into the other
+  // buffer, and the loads of those pieces of stage kt + 2. After the barrier
+  // the next stage's first operands are read from the other buffer while the
+  // second k-step's MFMAs run. Reads, stores and loads past the last stage
+  // move zeros or unused data and are never contracted.
+  bf16x8 a0[kFI], b0[kXJ], a1[kFI], b1[kXJ];
+  auto first_operands = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < kFI; ++t) a0[t] = rd_a(buf, 0, t);
+#pragma unroll
+    for (int t = 0; t < kXJ; ++t) b0[t] = rd_b(buf, 0, t);
+  };
+  auto stage = [&](int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < kFI; ++i) {
+      mfma_rows(i, i + 1, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < kFI / 2) {
+        a1[2 * i] = rd_a(buf, 1, 2 * i);
+        a1[2 * i + 1] = rd_a(buf, 1, 2 * i + 1);
+      } else {
+        b1[2 * i - kFI] = rd_b(buf, 1, 2 * i - kFI);
+        b1[2 * i - kFI + 1] = rd_b(buf, 1, 2 * i - kFI + 1);
+      }
+      store_piece(buf ^ 1, i);
+      load_piece(kt + 2, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    first_operands(buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(0, kFI, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   const int nk = a.d_model / kK;
-  load(0, sw[0], sx[0]);
-  load(1, sw[1], sx[1]);
-  store(0, sw[0], sx[0]);
-  load(2, sw[0], sx[0]);
+#pragma unroll
+  for (int i = 0; i < kPPW; ++i) load_piece(0, i);
+#pragma unroll
+  for (int i = 0; i < kPPW; ++i) store_piece(0, i);
+#pragma unroll
+  for (int i = 0; i < kPPW; ++i) load_piece(1, i);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    compute(0);
-    store(1, sw[1], sx[1]);
-    load(kt + 3, sw[1], sx[1]);
-    __syncthreads();
-    if (kt + 1 < nk) compute(1);
-    store(0, sw[0], sx[0]);
-    load(kt + 4, sw[0], sx[0]);
-    __syncthreads();
-  }
+  first_operands(0);
+  for (int kt = 0; kt < nk; ++kt) stage(kt, kt & 1);
+  // the last MFMAs' results are read below: wait out their latency
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 
   // Epilogue: accumulator element e of lane (g, c) in tile (i, j) is feature
   // 16 i + 4 g + e, token 16 j + c of the wave. It goes to a token-major bf16
-  // tile in LDS (the stage buffers are free after the last barrier); each
-  // token's 128 features are then read back as 16 chunks of 8 and stored.
+  // tile in LDS; each token's 128 features are then read back as 16 chunks
+  // of 8 and stored. After the last barrier the stage buffers only see reads
+  // of operands that are never used, so each wave may overwrite them with its
+  // own tile without another barrier.
   char* ep = lds + wave * (kWX * kEStr);
 #pragma unroll
   for (int i = 0; i < kFI; ++i)
@@ -206,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
       if (fr >= Fk) { fr -= Fk; seg = 3; } } }
   const int h = fr / a.d;
   const int dim = fr % a.d;
-#pragma unroll
+#pragma unroll 4
   for (int p = 0; p < kWX / kRPI; ++p) {
     const int r = kRPI * p + lane / kCH;
     const int m = X0 + kWX * wx + r;
