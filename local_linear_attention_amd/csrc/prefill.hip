@@ -50,7 +50,7 @@
 // e and e (r - c) are rounded once to fp16 and V is staged as fp16 (exact for
 // bf16 values of magnitude 2^-14 .. 65504), two products per value tile.
 // l and Bs sum the same rounded weights, so A / l is an exact weighted mean
-// under weights perturbed by at most 2^-11 of themselves; the probe
+// under weights perturbed by less than 2^-10 of themselves; the probe
 // reference c follows the running weighted mean of r (moved on the first
 // block and whenever a block's max jumps by more than 2^3), so the rounding
 // of e (r - c) stays small next to the weights that dominate a row. Measured
@@ -511,7 +511,7 @@ __device__ __forceinline__ void prefill_rows(
     // ---- weights e and e (r - c), each rounded once to fp16 (toward zero):
     // the A operands of the value MFMAs. l and Bs sum the rounded values, so
     // the weights that reach A and C are exactly those of l and Bs, and the
-    // rounding only perturbs each weight by 2^-11 of itself instead of
+    // rounding only perturbs each weight by less than 2^-10 of itself instead of
     // leaving A out of step with l.
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     uint32_t pw[4], fw[4];
