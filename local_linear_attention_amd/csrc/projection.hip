@@ -60,9 +60,12 @@ constexpr int kXJ = kWX / 16;            // MFMA tiles per wave along tokens
 constexpr int kPPW = kTileF * kK * 2 / 16 / kThreads;  // W pieces (16 bytes) per thread per stage
 constexpr int kPPX = kTileX * kK * 2 / 16 / kThreads;  // x pieces per thread per stage
 constexpr int kBuf = (kTileF + kTileX) * kStr;         // one LDS buffer: W tile then x tile
+constexpr int kRowsPerLoad = 1024 / kStr;  // rows one wave-wide 16-byte load into LDS fills
+constexpr int kLoads = (kTileF + kTileX) / kRowsPerLoad / (kThreads / 64);  // such loads per wave per stage
 constexpr int kEStr = kWF * 2 + 16;      // epilogue: bytes per token row (16-byte aligned)
-// LDS: the two stage buffers, reused by the epilogue's token-major tiles
-constexpr int kLds = 2 * kBuf > kNWF * kNWX * kWX * kEStr ? 2 * kBuf : kNWF * kNWX * kWX * kEStr;
+constexpr int kEHalf = kWX / 2;          // epilogue: tokens per pass
+static_assert(kRowsPerLoad == 8 && kLoads == 16, "direct loads: 8 rows each, 16 per wave and stage");
+static_assert(2 * kEHalf * kEStr <= kBuf, "two waves' epilogue halves must fit in one stage buffer");
 
 // acc += a b (v_mfma_f32_16x16x32_bf16) with the accumulator bound to the
 // accumulation registers. Left to itself the register allocator splits the
@@ -74,9 +77,15 @@ __device__ __forceinline__ void mfma_agpr(f32x4& acc, const bf16x8& a, const bf1
 }
 
 // One workgroup per CU (its 4 waves, one per SIMD, may use the whole
-// register file).
+// register file). DMA: stage loads go from global memory straight into LDS
+// (needs d_model a multiple of 128: the stage loop runs in static pairs);
+// otherwise through registers.
+template <bool DMA>
 __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  // The two stage buffers are separate objects, so the compiler can tell a
+  // read of one from a load still landing in the other.
+  __shared__ __attribute__((aligned(16))) char lds0[kBuf];
+  __shared__ __attribute__((aligned(16))) char lds1[kBuf];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
     sx[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, voff, soff, 0);
   };
   auto store_piece = [&](int buf, int i) {
-    char* base = lds + buf * kBuf + loff + i * (kThreads / 8) * kStr;
+    char* base = (buf ? lds1 : lds0) + loff + i * (kThreads / 8) * kStr;
     *reinterpret_cast<i32x4*>(base) = sw[i];
     *reinterpret_cast<i32x4*>(base + kTileF * kStr) = sx[i];
   };
@@ -144,13 +153,13 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
   // A operand of feature tile t in lane (g, c): feature row 16 t + c,
   // d_model 32 ks + 8 g .. + 7 of the stage; B operand of token tile t
   // likewise with token rows.
-  auto rd_a = [&](int buf, int ks, int t) {
+  auto rd_a = [&](const char* buf, int ks, int t) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(
-        lds + buf * kBuf + (kWF * wf + 16 * t + c) * kStr + swz(c, g + 4 * ks)));
+        buf + (kWF * wf + 16 * t + c) * kStr + swz(c, g + 4 * ks)));
   };
-  auto rd_b = [&](int buf, int ks, int t) {
+  auto rd_b = [&](const char* buf, int ks, int t) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(
-        lds + buf * kBuf + (kTileF + kWX * wx + 16 * t + c) * kStr + swz(c, g + 4 * ks)));
+        buf + (kTileF + kWX * wx + 16 * t + c) * kStr + swz(c, g + 4 * ks)));
   };
   auto mfma_rows = [&](int i0, int i1, const bf16x8 (&af)[kFI], const bf16x8 (&bx)[kXJ]) {
 #pragma unroll
@@ -159,70 +168,126 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
       for (int j = 0; j < kXJ; ++j) mfma_agpr(acc[i][j], af[i], bx[j]);
   };
 
-  // Software pipeline, one barrier per stage. On entry to stage kt the
+  // Software pipeline, one barrier per stage. On entry to stage kt its
   // first k-step's operands (a0, b0) are in registers. Each feature row of
-  // its MFMAs is followed by two reads of the second k-step's operands, the
-  // store of one staged W piece and one x piece (stage kt + 1) into the other
-  // buffer, and the loads of those pieces of stage kt + 2. After the barrier
-  // the next stage's first operands are read from the other buffer while the
-  // second k-step's MFMAs run. Reads, stores and loads past the last stage
-  // move zeros or unused data and are never contracted.
+  // the first k-step's MFMAs is followed by two reads of the second k-step's
+  // operands (and, staging through registers, the store of one W and one x
+  // piece of stage kt + 1 into the other buffer and the loads of those pieces
+  // of stage kt + 2). The barrier then publishes stage kt + 1; its first
+  // operands are read while the second k-step's MFMAs run (and, loading
+  // straight into LDS, stage kt + 2 is loaded between them into the buffer
+  // just left). Loads past the last stage move zeros or unused data (or
+  // repeat the last stage) and are never contracted.
   bf16x8 a0[kFI], b0[kXJ], a1[kFI], b1[kXJ];
-  auto first_operands = [&](int buf) {
+  auto first_operands = [&](const char* buf) {
 #pragma unroll
     for (int t = 0; t < kFI; ++t) a0[t] = rd_a(buf, 0, t);
 #pragma unroll
     for (int t = 0; t < kXJ; ++t) b0[t] = rd_b(buf, 0, t);
   };
-  auto stage = [&](int kt, int buf) {
-#pragma unroll
-    for (int i = 0; i < kFI; ++i) {
-      mfma_rows(i, i + 1, a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i < kFI / 2) {
-        a1[2 * i] = rd_a(buf, 1, 2 * i);
-        a1[2 * i + 1] = rd_a(buf, 1, 2 * i + 1);
-      } else {
-        b1[2 * i - kFI] = rd_b(buf, 1, 2 * i - kFI);
-        b1[2 * i - kFI + 1] = rd_b(buf, 1, 2 * i - kFI + 1);
-      }
-      store_piece(buf ^ 1, i);
-      load_piece(kt + 2, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    first_operands(buf ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_rows(0, kFI, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
   const int nk = a.d_model / kK;
+  // Direct loads: one wave-wide 16-byte load fills 1 KiB of LDS in lane
+  // order, i.e. rows r0 .. r0 + 7 of a stage with lane L at row r0 + L / 8,
+  // physical chunk L % 8; the lane fetches the logical chunk the swizzle
+  // puts there. Wave w issues the loads of row blocks w, w + 4, .. (half in
+  // W, half in x), so r0 / 8 has the parity of w and one lane offset serves
+  // all of them.
+  const int lrow = lane / 8;
+  const uint32_t dvoff = (uint32_t)lrow * KB + 16 * ((lane % 8) ^ lrow ^ (wave & 1));
+  auto direct_loads = [&](int kt, char* buf, int i0, int i1) {
 #pragma unroll
-  for (int i = 0; i < kPPW; ++i) load_piece(0, i);
+    for (int i = i0; i < i1; ++i) {
+      const bool isx = i >= kLoads / 2;
+      const int r0 = kRowsPerLoad * (wave + (kThreads / 64) * (isx ? i - kLoads / 2 : i));
+      const int soff = __builtin_amdgcn_readfirstlane(r0 * KB + kt * kK * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          isx ? xrs : wrs,
+          (__attribute__((address_space(3))) void*)(buf + (isx ? kTileF * kStr : 0) + r0 * kStr), 16,
+          dvoff, soff, 0, 0);
+    }
+  };
+  if constexpr (DMA) {
+    auto stage = [&](int kt, const char* cur, char* nxt) {
 #pragma unroll
-  for (int i = 0; i < kPPW; ++i) store_piece(0, i);
+      for (int i = 0; i < kFI; ++i) {
+        mfma_rows(i, i + 1, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < kFI / 2) {
+          a1[2 * i] = rd_a(cur, 1, 2 * i);
+          a1[2 * i + 1] = rd_a(cur, 1, 2 * i + 1);
+        } else {
+          b1[2 * i - kFI] = rd_b(cur, 1, 2 * i - kFI);
+          b1[2 * i - kFI + 1] = rd_b(cur, 1, 2 * i - kFI + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();  // its fence waits for this wave's loads of stage kt + 1
+      first_operands(nxt);  // past the last stage: unused
+      __builtin_amdgcn_sched_barrier(0);
+      const int kl = min(kt + 2, nk - 1);
 #pragma unroll
-  for (int i = 0; i < kPPW; ++i) load_piece(1, i);
-  __syncthreads();
-  first_operands(0);
-  for (int kt = 0; kt < nk; ++kt) stage(kt, kt & 1);
+      for (int i = 0; i < kFI; ++i) {
+        direct_loads(kl, const_cast<char*>(cur), 2 * i, 2 * i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(i, i + 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    direct_loads(0, lds0, 0, kLoads);
+    __syncthreads();
+    first_operands(lds0);
+    direct_loads(min(1, nk - 1), lds1, 0, kLoads);
+    for (int kt = 0; kt < nk; kt += 2) {  // nk is even
+      stage(kt, lds0, lds1);
+      stage(kt + 1, lds1, lds0);
+    }
+    __syncthreads();  // no load still lands in a buffer the epilogue reuses
+  } else {
+    auto stage = [&](int kt, int buf) {
+      const char* cur = buf ? lds1 : lds0;
+#pragma unroll
+      for (int i = 0; i < kFI; ++i) {
+        mfma_rows(i, i + 1, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < kFI / 2) {
+          a1[2 * i] = rd_a(cur, 1, 2 * i);
+          a1[2 * i + 1] = rd_a(cur, 1, 2 * i + 1);
+        } else {
+          b1[2 * i - kFI] = rd_b(cur, 1, 2 * i - kFI);
+          b1[2 * i - kFI + 1] = rd_b(cur, 1, 2 * i - kFI + 1);
+        }
+        store_piece(buf ^ 1, i);
+        load_piece(kt + 2, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      first_operands(buf ? lds0 : lds1);  // past the last stage: unused
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_rows(0, kFI, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int i = 0; i < kPPW; ++i) load_piece(0, i);
+#pragma unroll
+    for (int i = 0; i < kPPW; ++i) store_piece(0, i);
+#pragma unroll
+    for (int i = 0; i < kPPW; ++i) load_piece(1, i);
+    __syncthreads();
+    first_operands(lds0);
+    for (int kt = 0; kt < nk; ++kt) stage(kt, kt & 1);
+  }
   // the last MFMAs' results are read below: wait out their latency
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 
   // Epilogue: accumulator element e of lane (g, c) in tile (i, j) is feature
-  // 16 i + 4 g + e, token 16 j + c of the wave. It goes to a token-major bf16
-  // tile in LDS; each token's 128 features are then read back as 16 chunks
-  // of 8 and stored. After the last barrier the stage buffers only see reads
-  // of operands that are never used, so each wave may overwrite them with its
-  // own tile without another barrier.
-  char* ep = lds + wave * (kWX * kEStr);
-#pragma unroll
-  for (int i = 0; i < kFI; ++i)
-#pragma unroll
-    for (int j = 0; j < kXJ; ++j) {
-      const uint2 val = {pack_bf16(acc[i][j][0], acc[i][j][1]), pack_bf16(acc[i][j][2], acc[i][j][3])};
-      *reinterpret_cast<uint2*>(ep + (16 * j + c) * kEStr + (16 * i + 4 * g) * 2) = val;
-    }
+  // 16 i + 4 g + e, token 16 j + c of the wave. In two passes of 64 tokens it
+  // goes to a token-major bf16 tile in LDS (waves 0 and 1 in one stage
+  // buffer, waves 2 and 3 in the other); each token's 128 features are then
+  // read back as 16 chunks of 8 and stored. After the last barrier the stage
+  // buffers only see reads of operands that are never used and no load
+  // lands in them, so each wave may overwrite its part (the parts are
+  // disjoint) without another barrier.
+  char* ep = ((wave >> 1) ? lds1 : lds0) + (wave & 1) * (kEHalf * kEStr);
   constexpr int kCH = kWF / 8;   // 16-byte chunks per token row
   constexpr int kRPI = 64 / kCH;  // token rows per pass of the wave
   const int ch = lane % kCH;
@@ -234,23 +299,34 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
       if (fr >= Fk) { fr -= Fk; seg = 3; } } }
   const int h = fr / a.d;
   const int dim = fr % a.d;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int i = 0; i < kFI; ++i)
+#pragma unroll
+      for (int j = 0; j < kXJ / 2; ++j) {
+        const f32x4 v = acc[i][j + half * (kXJ / 2)];
+        const uint2 val = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        *reinterpret_cast<uint2*>(ep + (16 * j + c) * kEStr + (16 * i + 4 * g) * 2) = val;
+      }
 #pragma unroll 4
-  for (int p = 0; p < kWX / kRPI; ++p) {
-    const int r = kRPI * p + lane / kCH;
-    const int m = X0 + kWX * wx + r;
-    if (m >= M || f >= N) continue;
-    const int b = m / a.T;
-    const int t = m % a.T;
-    const i32x4 val = *reinterpret_cast<const i32x4*>(ep + r * kEStr + 16 * ch);
-    __bf16* dst;
-    if (seg == 0 || seg == 3) {
-      dst = static_cast<__bf16*>(seg == 0 ? a.q : a.rho) + (((size_t)b * a.H_q + h) * a.T + t) * a.d + dim;
-    } else {
-      const int pos = (a.past_lens ? min(max(a.past_lens[b], 0), a.S_max) : 0) + t;
-      if (pos >= a.S_max) continue;
-      dst = static_cast<__bf16*>(seg == 1 ? a.k : a.v) + (((size_t)b * a.H_kv + h) * a.S_max + pos) * a.d + dim;
+    for (int p = 0; p < kEHalf / kRPI; ++p) {
+      const int r = kRPI * p + lane / kCH;
+      const int m = X0 + kWX * wx + kEHalf * half + r;
+      if (m >= M || f >= N) continue;
+      const int b = m / a.T;
+      const int t = m % a.T;
+      const i32x4 val = *reinterpret_cast<const i32x4*>(ep + r * kEStr + 16 * ch);
+      __bf16* dst;
+      if (seg == 0 || seg == 3) {
+        dst = static_cast<__bf16*>(seg == 0 ? a.q : a.rho) + (((size_t)b * a.H_q + h) * a.T + t) * a.d + dim;
+      } else {
+        const int pos = (a.past_lens ? min(max(a.past_lens[b], 0), a.S_max) : 0) + t;
+        if (pos >= a.S_max) continue;
+        dst = static_cast<__bf16*>(seg == 1 ? a.k : a.v) + (((size_t)b * a.H_kv + h) * a.S_max + pos) * a.d + dim;
+      }
+      *reinterpret_cast<i32x4*>(dst) = val;
     }
-    *reinterpret_cast<i32x4*>(dst) = val;
   }
 }
 
@@ -260,7 +336,10 @@ hipError_t launch_projection(const ProjArgs& a, hipStream_t st) {
   const int N = (2 * a.H_q + 2 * a.H_kv) * a.d;
   const int M = a.B * a.T;
   dim3 grid((N + kTileF - 1) / kTileF, (M + kTileX - 1) / kTileX);
-  hipLaunchKernelGGL(proj_kernel, grid, dim3(kThreads), 0, st, a);
+  if (a.d_model % (2 * kK) == 0)
+    hipLaunchKernelGGL(proj_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(proj_kernel<false>, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
