@@ -22,13 +22,17 @@
 // of 128 x 64 per SIMD (whose operand reads and staging writes kept the LDS
 // as busy as the matrix pipe). K (d_model) advances 64 at a time through
 // double-buffered LDS (chunks XOR-swizzled per row against bank conflicts).
-// With one wave per SIMD nothing else hides a wave's
-// LDS and global latency, so the wave pipelines its own: between the rows
-// of one k-step's MFMAs it reads the next k-step's operands, stores the next
-// stage from registers into the other buffer and loads the stage after it,
-// and the next stage's first operands are read under the current stage's
-// last MFMAs (one barrier per stage, between its two k-steps). Loads past
-// x's or W's rows come back as zeros (range-checked buffer loads).
+// With one wave per SIMD nothing else hides a wave's LDS and global latency,
+// so the wave pipelines its own: between the rows of one k-step's MFMAs it
+// reads the next k-step's operands, and the next stage's first operands are
+// read under the current stage's last MFMAs (one barrier per stage, between
+// its two k-steps). On gfx950 every memory instruction a wave issues holds
+// up its own MFMAs, so when d_model is a multiple of 128 the stages are
+// loaded straight from global memory into LDS (buffer loads with the LDS
+// flag, between the second k-step's MFMAs): no staging registers and no LDS
+// store instructions (7% faster). Otherwise each stage goes through
+// registers, stored into the other buffer between the first k-step's MFMAs.
+// Loads past x's or W's rows come back as zeros (range-checked buffer loads).
 //
 // Epilogue. Each wave writes its tile to LDS token-major, then every token's
 // 128 features (consecutive dims of one or two heads) leave as 16-byte stores,
