@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
     }
   };
   if constexpr (DMA) {
-    auto stage = [&](int kt, const char* cur, char* nxt) {
+    auto stage = [&](int kt, char* cur, char* nxt) {
 #pragma unroll
       for (int i = 0; i < kFI; ++i) {
         mfma_rows(i, i + 1, a0, b0);
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
       const int kl = min(kt + 2, nk - 1);
 #pragma unroll
       for (int i = 0; i < kFI; ++i) {
-        direct_loads(kl, const_cast<char*>(cur), 2 * i, 2 * i + 2);
+        direct_loads(kl, cur, 2 * i, 2 * i + 2);
         __builtin_amdgcn_sched_barrier(0);
         mfma_rows(i, i + 1, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
