@@ -355,8 +355,9 @@ size_t parallax_prefill_backward_workspace_size(int B, int H_q, int T, int d);
  *             of each KV head (keys j >= seq_lens[b] are 0).
  * Every output is written in full. Rows of dout at or past seq_lens[b] are
  * ignored. `workspace` (device, 16-byte aligned, caller-owned, at least
- * parallax_prefill_backward_workspace_size bytes) is overwritten. Three
- * launches on `stream`, asynchronous; nothing is allocated. Errors as
+ * parallax_prefill_backward_workspace_size bytes) is scratch: the first
+ * launch writes its entries for rows below seq_lens[b] and the second reads
+ * them. Two launches on `stream`, asynchronous; nothing is allocated. Errors as
  * parallax_prefill, plus PARALLAX_ERR_WORKSPACE for a short workspace; on an
  * error nothing is launched. Deterministic: no atomics, fixed reduction
  * order. */

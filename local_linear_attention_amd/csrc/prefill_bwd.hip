@@ -21,15 +21,16 @@
 // u = (r - c_t) - (rbar - c_t). The weights are recomputed from the saved
 // log2-sum-exp, so no T x T matrix is stored.
 //
-// Three launches:
-//  1. prep: splits dO (fp32) into bf16 high and low parts and forms G and Dt
-//     per row (from the saved mu_v and the output).
-//  2. dq/drho: per 128 query rows (8 waves x 16 rows), over key blocks of 32
-//     staged in LDS (as the forward). s, r - c and g come from
-//     v_mfma_f32_16x16x32_bf16 in the forward's transposed layout; ds and dr
-//     (fp32, split into bf16 high and low parts) contract with K, whose
-//     operand the transposing LDS load reads straight from the row-major tile.
-//  3. dk/dv: per 128 keys (8 waves x 16 keys) of one KV head, over the
+// Two launches:
+//  1. dq/drho: per 128 query rows (8 waves x 16 rows), over key blocks of 32
+//     staged in LDS (as the forward). Each lane first splits its row's dO
+//     (fp32) into bf16 high and low parts and forms the row's G and Dt (from
+//     the saved mu_v and the output), and leaves both in the workspace for
+//     the second launch. s, r - c and g come from v_mfma_f32_16x16x32_bf16
+//     in the forward's transposed layout; ds and dr (fp32, split into bf16
+//     high and low parts) contract with K, whose operand the transposing LDS
+//     load reads straight from the row-major tile.
+//  2. dk/dv: per 128 keys (8 waves x 16 keys) of one KV head, over the
 //     query-row blocks of 32 of every head of its group that see those keys,
 //     with q, rho, dO (high, low) and the row statistics staged in LDS.
 //     s, r - c, g come out with keys as columns, so each lane holds one key
@@ -137,51 +138,7 @@ __device__ __forceinline__ bf16x8 load8(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. prep: dO -> (high, low) bf16 and per-row (G, Dt); rows >= n get zeros.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(
-    const float* __restrict__ dout, const float* __restrict__ out, const float* __restrict__ mu,
-    const int32_t* __restrict__ seq_lens, __bf16* __restrict__ dhi, __bf16* __restrict__ dlo,
-    float2* __restrict__ gd, int H_q, int T, long long rows) {
-  constexpr int PARTS = D / 8;  // threads per row, 8 dims each
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gid / PARTS;
-  const int part = (int)(gid % PARTS);
-  const bool in = row < rows;
-  const long long r = in ? row : 0;
-  const int t = (int)(r % T);
-  const int b = (int)(r / ((long long)T * H_q));
-  const bool live = in && t < min(max(seq_lens[b], 0), T);
-  const size_t off = (size_t)r * D + 8 * part;
-  float x[8], gs = 0.f, ds = 0.f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float4 a = reinterpret_cast<const float4*>(dout + off)[h];
-    const float4 o = reinterpret_cast<const float4*>(out + off)[h];
-    const float4 m = reinterpret_cast<const float4*>(mu + off)[h];
-    x[4 * h + 0] = live ? a.x : 0.f;
-    x[4 * h + 1] = live ? a.y : 0.f;
-    x[4 * h + 2] = live ? a.z : 0.f;
-    x[4 * h + 3] = live ? a.w : 0.f;
-    gs += x[4 * h] * m.x + x[4 * h + 1] * m.y + x[4 * h + 2] * m.z + x[4 * h + 3] * m.w;
-    ds += x[4 * h] * o.x + x[4 * h + 1] * o.y + x[4 * h + 2] * o.z + x[4 * h + 3] * o.w;
-  }
-#pragma unroll
-  for (int sh = PARTS / 2; sh >= 1; sh >>= 1) {
-    gs += __shfl_xor(gs, sh);
-    ds += __shfl_xor(ds, sh);
-  }
-  bf16x8 hi, lo;
-  split8(x, hi, lo);
-  if (in) {
-    *reinterpret_cast<bf16x8*>(dhi + off) = hi;
-    *reinterpret_cast<bf16x8*>(dlo + off) = lo;
-    if (part == 0) gd[r] = float2{gs, ds};
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dq, drho: one row block (128 rows from rb * 128) of one (b, h).
+// 1. dq, drho: one row block (128 rows from rb * 128) of one (b, h).
 template <int D>
 __device__ __forceinline__ void dq_rows(const BwdArgs& a, int rb, int h, int b,
                                         char (&lds)[2][2][Bw<D>::TILE]) {
@@ -213,9 +170,15 @@ __device__ __forceinline__ void dq_rows(const BwdArgs& a, int rb, int h, int b,
   }
 
   // Row operands (B of the transposed products): row my_row, dims 32 kk + 8 g.
+  // dO comes in fp32 and is split here into its bf16 high and low parts; the
+  // row's G = dO.mu_v and Dt = dO.out are summed over this lane's dims and
+  // the row's 4 lanes (g). The parts and (G, Dt) also go to the workspace,
+  // where the dk/dv launch that follows reads them (rows below n only; every
+  // such row belongs to exactly one workgroup of this launch).
   const bool live = my_row < n;
   const size_t roff = (qbase + (live ? my_row : 0)) * D + 8 * g;
   bf16x8 qop[P::KST], rop[P::KST], dhop[P::KST], dlop[P::KST];
+  float Gr = 0.f, Dr = 0.f;
 #pragma unroll
   for (int kk = 0; kk < P::KST; ++kk) {
     const bf16x8 z = __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0});
@@ -223,18 +186,38 @@ __device__ __forceinline__ void dq_rows(const BwdArgs& a, int rb, int h, int b,
                          static_cast<const __bf16*>(a.q) + roff + 32 * kk)) : z;
     rop[kk] = live ? load8(reinterpret_cast<const char*>(
                          static_cast<const __bf16*>(a.rho) + roff + 32 * kk)) : z;
-    dhop[kk] = live ? load8(reinterpret_cast<const char*>(a.dhi + roff + 32 * kk)) : z;
-    dlop[kk] = live ? load8(reinterpret_cast<const char*>(a.dlo + roff + 32 * kk)) : z;
+    float x[8];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const size_t o4 = roff + 32 * kk + 4 * h2;
+      const float4 dv4 = live ? *reinterpret_cast<const float4*>(a.dout + o4) : float4{0.f, 0.f, 0.f, 0.f};
+      const float4 m4 = live ? *reinterpret_cast<const float4*>(a.mu + o4) : float4{0.f, 0.f, 0.f, 0.f};
+      const float4 o44 = live ? *reinterpret_cast<const float4*>(a.out + o4) : float4{0.f, 0.f, 0.f, 0.f};
+      x[4 * h2 + 0] = dv4.x;
+      x[4 * h2 + 1] = dv4.y;
+      x[4 * h2 + 2] = dv4.z;
+      x[4 * h2 + 3] = dv4.w;
+      Gr += dv4.x * m4.x + dv4.y * m4.y + dv4.z * m4.z + dv4.w * m4.w;
+      Dr += dv4.x * o44.x + dv4.y * o44.y + dv4.z * o44.z + dv4.w * o44.w;
+    }
+    split8(x, dhop[kk], dlop[kk]);
+    if (live) {
+      *reinterpret_cast<bf16x8*>(a.dhi + roff + 32 * kk) = dhop[kk];
+      *reinterpret_cast<bf16x8*>(a.dlo + roff + 32 * kk) = dlop[kk];
+    }
   }
-  float lse2 = 0.f, crow = 0.f, rbc = 0.f, Gr = 0.f, Dr = 0.f;
+  // the row's 4 lanes are c, c + 16, c + 32, c + 48
+  Gr += __shfl_xor(Gr, 16);
+  Dr += __shfl_xor(Dr, 16);
+  Gr += __shfl_xor(Gr, 32);
+  Dr += __shfl_xor(Dr, 32);
+  if (live && g == 0) a.gd[qbase + my_row] = float2{Gr, Dr};
+  float lse2 = 0.f, crow = 0.f, rbc = 0.f;
   if (live) {
     const float4 st = a.stats[qbase + my_row];
-    const float2 q2 = a.gd[qbase + my_row];
     lse2 = st.x;
     crow = st.y;
     rbc = st.z;
-    Gr = q2.x;
-    Dr = q2.y;
   }
   const f32x4 rinit = {-crow, -crow, -crow, -crow};
 
@@ -392,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dk, dv: one key block (128 keys from kb * 128) of one (b, KV head).
+// 2. dk, dv: one key block (128 keys from kb * 128) of one (b, KV head).
 struct RowStat {
   float lse2, c, rbc, G, Dt, pad0, pad1, pad2;
 };
@@ -647,15 +630,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
-  const long long rows = (long long)a.B * a.H_q * a.T;
-  const long long threads = rows * (D / 8);
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     a.dout, a.out, a.mu, a.seq_lens, a.dhi, a.dlo, a.gd, a.H_q, a.T, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nrb = (a.T + kQRows - 1) / kQRows;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((nrb + 1) / 2, a.H_q, a.B), dim3(kThreads), 0, st, a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (a.S_max + kKKeys - 1) / kKKeys;
   hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3((nkb + 1) / 2, a.H_kv, a.B), dim3(kThreads), 0, st, a);
