@@ -328,7 +328,7 @@ def bench_prefill(w, steps, warmup, seed=None, keep=None, flush=None):
 
 
 def bench_backward(w, steps, warmup, seed=None, flush=None):
-    """Causal-prefill backward (prep + dq/drho + dk/dv launches) per step, and
+    """Causal-prefill backward (dq/drho and dk/dv launches) per step, and
     the training forward that saves mu_v and the row statistics."""
     import torch
 
