@@ -128,6 +128,22 @@ def test_strong_probe(rho_std, scale):
     check(w, seq_lens=[384, 301])
 
 
+def test_strong_probe_head_dim_64():
+    """The fp16 value weights at d = 64 with a probe 20x the workload's and a
+    sharp softmax."""
+    w = replace_shape(SMALL, d=64, q_std=64 ** -0.25, k_std=64 ** -0.25, rho_std=1.0, scale=8.0,
+                      T=384)
+    check(w, seq_lens=[384, 257])
+
+
+@pytest.mark.parametrize("v_std", [1e-2, 300.0])
+def test_value_scale(v_std):
+    """V is staged as fp16: values 100x smaller or 300x larger than the
+    workload's stay inside fp16's normal range (2^-14 .. 65504), and the
+    result scales with them."""
+    check(replace_shape(SMALL, v_std=v_std), seq_lens=[200, 171])
+
+
 def test_unscaled_dot_reading():
     check(replace_shape(SMALL, scale=128 ** -0.5))
 
