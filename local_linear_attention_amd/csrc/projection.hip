@@ -241,10 +241,14 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
     __syncthreads();
     first_operands(lds0);
     direct_loads(min(1, nk - 1), lds1, 0, kLoads);
-    for (int kt = 0; kt < nk; kt += 2) {  // nk is even
+    // A loop that may run zero times made the compiler zero the 256
+    // accumulators twice (before and after its trip-count test).
+    int kt = 0;
+    do {  // nk is even and at least 2
       stage(kt, lds0, lds1);
       stage(kt + 1, lds1, lds0);
-    }
+      kt += 2;
+    } while (kt < nk);
     __syncthreads();  // no load still lands in a buffer the epilogue reuses
   } else {
     auto stage = [&](int kt, int buf) {
@@ -278,7 +282,10 @@ __global__ __launch_bounds__(kThreads, 1) void proj_kernel(ProjArgs a) {
     for (int i = 0; i < kPPW; ++i) load_piece(1, i);
     __syncthreads();
     first_operands(lds0);
-    for (int kt = 0; kt < nk; ++kt) stage(kt, kt & 1);
+    int kt = 0;
+    do {  // nk is at least 1
+      stage(kt, kt & 1);
+    } while (++kt < nk);
   }
   // the last MFMAs' results are read below: wait out their latency
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
