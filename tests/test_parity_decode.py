@@ -193,6 +193,32 @@ def test_two_phase_equals_one_shot():
     assert np.array_equal(out.cpu().numpy(), one)
 
 
+@pytest.mark.parametrize("ns,H_q", [(2, 16), (3, 16), (5, 16), (8, 16), (12, 16), (16, 16), (32, 16),
+                                     (5, 64), (12, 64)])
+def test_two_phase_equals_one_shot_split_counts(ns, H_q):
+    """Fused and two-phase merges agree bit for bit whatever the split count.
+
+    The merging workgroup batches its record loads by the number of splits
+    that hold keys (up to 8 at a time); the combine kernel does the same
+    with other item widths. Lengths here give streams with 1 up to ns
+    splits, so every batch size and a second batch are exercised.
+    """
+    w = replace_shape(WORKLOADS[2], B=3, H_q=H_q, S_max=4096)
+    dev = to_dev(make_decode_inputs(w, seq_lens=[4096, 1029, 97]))
+    nsr, _ = pa.decode_plan(w.B, w.H_q, w.H_kv, w.d, w.S_max, ns)
+    assert nsr == (11 if ns == 12 else ns)  # the plan's chunks are multiples of 128 keys
+    ws = torch.empty(pa.decode_workspace_size(w.B, w.H_q, w.d, nsr) // 4, device="cuda")
+    out = torch.empty(w.B, w.H_q, w.d, device="cuda")
+    pa.decode_partial(dev["q"], dev["rho"], dev["k_cache"], dev["v_cache"], dev["seq_lens"],
+                      dev["scale"], ws, num_splits=ns)
+    pa.decode_combine(dev["seq_lens"], out, ws, H_kv=w.H_kv, S_max=w.S_max, num_splits=ns)
+    one = run_decode(dev, ns)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), one)
+    ref = oracle_all(dev)
+    assert rel_err(one, ref) < TOL
+
+
 def test_out_of_range_seq_lens_are_clamped():
     w = replace_shape(WORKLOADS[2], B=2, S_max=256)
     cpu = make_decode_inputs(w, seq_lens=[256, 0], nan_pad=False)
