@@ -27,8 +27,8 @@ they were taken on are unchanged.
 Workloads: the GQA decode line (also at head dim 64), single-head fp32,
 ragged batch, 128K-context split-KV decode, 64 query heads on 8 KV heads,
 multi-token decode (2, 3 and 4 new tokens), causal prefill, chunked prefill
-(1024 new rows after 3072 cached tokens, and 32 or 64 new rows after the
-rest of a 4096-key cache at the GQA decode shape), the prefill backward and
+(1024 new rows after 3072 cached tokens, and 32, 64, 128 or 256 new rows
+after the rest of a 4096-key cache at the GQA decode shape), the prefill backward and
 the fused q/k/v/rho projection. The `cpu_baseline` leg times the fp64 oracle on a
 bounded sample of the GQA decode workload on the host cores.
 
@@ -654,7 +654,7 @@ def workload_registry(steps, warmup, flush, prefill_keep=None):
                                                   keep=prefill_keep, flush=flush)
     reg["chunked-prefill"] = lambda: bench_chunked(CHUNK_WORKLOAD, max(5, steps // 10), 10,
                                                    flush=flush)
-    for T in (32, 64):
+    for T in (32, 64, 128, 256):
         wc = replace_shape(CHUNK_WORKLOAD, name=f"short-chunk-prefill-T{T}", B=8, T=T,
                            past=4096 - T, H_q=16, H_kv=8, d=128)
         reg[f"short-chunk-prefill-T{T}"] = (lambda wc=wc: bench_chunked(

@@ -279,9 +279,10 @@ parallax_status_t parallax_prefill(const void* q, const void* rho, const void* k
  *   out         [B, H_q, T, d]       fp32, written in full
  * Only dtype PARALLAX_BF16 is built. Passage and precision as
  * parallax_prefill, with the chunk's rows placed after the cached tokens
- * (the causal reading of continuing a sequence). Chunks of at most 64 rows
- * split each row block's keys into 4 ranges whose partial states are merged
- * exactly (rescaled to a common max and moved to a common probe reference).
+ * (the causal reading of continuing a sequence). Chunks of at most 256 rows
+ * split each row block's keys into 4 ranges (up to 64 rows) or 2 ranges
+ * whose partial states are merged exactly (rescaled to a common max and moved
+ * to a common probe reference).
  * Errors as parallax_prefill, plus PARALLAX_ERR_NULL_POINTER for a NULL
  * past_lens and PARALLAX_ERR_MISALIGNED for a past_lens not 4-byte aligned.
  */

@@ -37,12 +37,13 @@
 // a heavy (late) and a light (early) row block, so every workgroup carries
 // the same causal work.
 //
-// Short chunks (at most 64 rows, e.g. a few new tokens after a long cache)
-// would leave most of the chip idle with 128-row blocks. They take 16-row
-// (up to 32 rows) or 32-row blocks, one per workgroup, and split each row
-// block's keys into 4 contiguous ranges: a step stages the next block of
-// every range, each of the first 4 TL waves (TL tiles of 16 rows per range)
-// contracts its own range's block, the remaining waves only help stage, and
+// Short chunks (at most 256 rows, e.g. a few new tokens after a long cache)
+// would leave most of the chip idle with 128-row blocks paired per
+// workgroup. They take 16-row (up to 32 rows), 32-row (up to 64) or 64-row
+// blocks, one per workgroup, and split each row block's keys into NS
+// contiguous ranges (4, 4 and 2): a step stages the next block of every
+// range, each of the first NS TL waves (TL tiles of 16 rows per range)
+// contracts its own range's block, any remaining waves only help stage, and
 // at the end the ranges' (m, l, Bs, c, A, C) merge in LDS into the range-0
 // waves. Each step's loads are issued two steps ahead.
 //
@@ -164,6 +165,10 @@ __device__ __forceinline__ void prefill_rows(
   constexpr int SLOTS = slots_for(NS);
   constexpr int TILES = TL;          // 16-row tiles
   constexpr int ROWS = 16 * TILES;   // query rows of the workgroup
+  // the range merge reuses the stage buffers: per-row states of every range
+  // and the accumulators of ranges 1.. (2 DPL f32x4 per lane)
+  static_assert(NS == 1 || (NS * TILES * 16 * 4 + (NS - 1) * TILES * 64 * 2 * P::DPL * 4) * 4 <=
+                               (int)sizeof(kv_lds), "range merge fits in the stage buffers");
   const int hk = h / G;
   // Row t of this chunk sits at position past + t of the sequence and sees
   // keys 0 .. past + t of the cache; rows t >= n are zero.
@@ -774,11 +779,14 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
 
 // Inference forms by chunk length: up to 32 rows, four key ranges of one
 // 16-row tile (half the waves contract, all of them stage keys); up to 64,
-// four ranges of two tiles; longer chunks, one range of eight tiles.
+// four ranges of two tiles; up to 256, two ranges of four tiles (64-row
+// blocks: at 8 sequences of 16 heads, 256 to 512 workgroups where paired
+// 128-row blocks give 128); longer chunks, one range of eight tiles.
 template <int D>
 hipError_t launch_prefill_infer(const PrefillArgs& a, hipStream_t st) {
   if (a.T <= 32) return launch_prefill_t<D, false, 4, 1>(a, st);
   if (a.T <= 64) return launch_prefill_t<D, false, 4, 2>(a, st);
+  if (a.T <= 256) return launch_prefill_t<D, false, 2, 4>(a, st);
   return launch_prefill_t<D, false, 1, kWaves>(a, st);
 }
 

@@ -102,25 +102,27 @@ def test_multi_token_decode(T):
     check(replace_shape(SMALL, T=T, past=2000))
 
 
-@pytest.mark.parametrize("T", [1, 16, 17, 32, 33, 48, 64, 65, 127])
+@pytest.mark.parametrize("T", [1, 16, 17, 32, 33, 48, 64, 65, 127, 128, 129, 200, 256, 257])
 def test_short_chunks(T):
-    """Chunks of up to 64 rows split the keys of each row block into 4 ranges
-    and merge the ranges' states (16-row blocks up to 32 rows, 32-row blocks
-    up to 64); 65 and 127 rows take the one-range path."""
+    """Chunks of up to 256 rows split the keys of each row block into ranges
+    and merge the ranges' states: 4 ranges of 16-row blocks up to 32 rows,
+    4 of 32-row blocks up to 64, 2 of 64-row blocks up to 256; 257 rows take
+    the one-range path."""
     check(replace_shape(SMALL, T=T, past=2000))
 
 
-@pytest.mark.parametrize("T", [9, 32, 50])
+@pytest.mark.parametrize("T", [9, 32, 50, 100, 256])
 def test_short_chunks_d64(T):
     w = replace_shape(SMALL, T=T, past=1500, d=64, q_std=64 ** -0.25, k_std=64 ** -0.25)
     check(w)
 
 
-def test_short_chunks_ragged():
+@pytest.mark.parametrize("T", [48, 160])
+def test_short_chunks_ragged(T):
     """Split key ranges with chunk lengths and pasts that differ per sequence
     (one empty chunk, one whose keys fit in the first range)."""
-    w = replace_shape(SMALL, B=4, T=48)
-    check(w, past_lens=[1900, 0, 37, 700], chunk_lens=[48, 17, 0, 31], S_max=2000)
+    w = replace_shape(SMALL, B=4, T=T)
+    check(w, past_lens=[1900, 0, 37, 700], chunk_lens=[T, 17, 0, T - 17], S_max=2000 + T)
 
 
 def test_ragged_past_and_chunk_lengths():
@@ -158,7 +160,14 @@ def test_no_past_equals_prefill():
 
 
 def test_chunks_reproduce_full_prefill():
-    """Prefilling a sequence in three chunks gives the full prefill's rows."""
+    """Prefilling a sequence in three chunks gives the full prefill's rows.
+
+    Chunks of up to 256 rows split their keys into ranges, each with its own
+    running max and probe reference for the fp16 value weights, so their
+    rounding differs from the one-range full prefill's (each weight within
+    2^-10 of itself either way): rows agree to the per-row bar both meet
+    against the oracle, not bit for bit.
+    """
     w = replace_shape(WORKLOADS[5], B=1, T=384, H_q=4, H_kv=2)
     dev = to_dev(make_prefill_inputs(w))
     full = pa.prefill(dev["q"], dev["rho"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"])
@@ -171,7 +180,9 @@ def test_chunks_reproduce_full_prefill():
         torch.cuda.synchronize()
         a = out.cpu().numpy()[0]
         b = full.cpu().numpy()[0, :, p0:p1]
-        assert np.abs(a - b).max() <= 1e-4 * np.abs(b).max()
+        err = max(rel_err(a[h], b[h]) for h in range(w.H_q))
+        print(f"   rows {p0}..{p1 - 1}: max rel difference {err:.3e}", flush=True)
+        assert err < TOL
 
 
 @pytest.mark.slow
