@@ -135,11 +135,13 @@ def test_negative_and_zero_scale(scale):
     check(replace_shape(SMALL, scale=scale))
 
 
+@pytest.mark.parametrize("T", [40, 130, 256])
 @pytest.mark.parametrize("rho_std,scale", [(1.0, 1.0), (1.0, 8.0)])
-def test_strong_probe(rho_std, scale):
+def test_strong_probe(rho_std, scale, T):
     """Probes 20x the workload's, with a long past: the fp16 value weights are
-    most exposed where the covariance correction dominates the output."""
-    check(replace_shape(SMALL, rho_std=rho_std, scale=scale, past=1500, T=130))
+    most exposed where the covariance correction dominates the output (four
+    key ranges at 40 rows, two at 130 and 256)."""
+    check(replace_shape(SMALL, rho_std=rho_std, scale=scale, past=1500, T=T))
 
 
 def test_group_sizes_and_head_dim_64():
