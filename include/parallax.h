@@ -73,7 +73,14 @@ typedef enum {
   PARALLAX_ERR_TOO_LARGE = 7     /* beyond the built-in scratch of parallax_decode_noalloc */
 } parallax_status_t;
 
-typedef enum { PARALLAX_BF16 = 0, PARALLAX_F32 = 1 } parallax_dtype_t;
+typedef enum {
+  PARALLAX_BF16 = 0,
+  PARALLAX_F32 = 1,
+  /* not dtypes: they give the type the range of int, so that any int a
+     caller passes is a value of it (and is refused as unsupported) */
+  PARALLAX_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  PARALLAX_DTYPE_RANGE_MAX_ = 0x7fffffff
+} parallax_dtype_t;
 
 /* PARALLAX_ABI_VERSION of the built library. */
 int parallax_abi_version(void);
@@ -107,7 +114,8 @@ parallax_status_t parallax_decode_plan(int B, int H_q, int H_kv, int d, int S_ma
  * (2 d + 4) values (running max, weight sum, probe sum, probe reference, and
  * two d-vectors) per (b, h_q, split), followed by B * H_q 32-bit arrival
  * counters (rounded up to 16 bytes). 0 if num_splits == 1 (the kernel then
- * finalises directly) or on a bad shape.
+ * finalises directly), on a bad shape, or when the workspace would reach
+ * 2^62 bytes (every call refuses such a plan with PARALLAX_ERR_UNSUPPORTED).
  *
  * The counters are used by parallax_decode only. They must be zero before the
  * first parallax_decode call on a workspace (allocate it zeroed, or clear the
@@ -146,8 +154,9 @@ size_t parallax_decode_workspace_size(int B, int H_q, int d, int num_splits);
  * Errors: PARALLAX_ERR_NULL_POINTER (q, rho, a cache, seq_lens or out NULL);
  * PARALLAX_ERR_BAD_SHAPE (a size <= 0, H_q % H_kv != 0, num_splits < 0, scale
  * not finite); PARALLAX_ERR_UNSUPPORTED (d not in {64, 128}, dtype not bf16
- * or fp32, B > 65535, a (b, h_kv) slice of 2 GiB or more, more than 65535
- * splits); PARALLAX_ERR_MISALIGNED (a tensor or the workspace not 16-byte
+ * or fp32, B > 65535, a (b, h_kv) slice or one sequence's [H_q, d] queries
+ * of 2 GiB or more, more than 65535 splits, a workspace of 2^62 bytes or
+ * more); PARALLAX_ERR_MISALIGNED (a tensor or the workspace not 16-byte
  * aligned, seq_lens not 4-byte aligned); PARALLAX_ERR_WORKSPACE (workspace
  * NULL or smaller than parallax_decode_workspace_size for the plan);
  * PARALLAX_ERR_HIP (device query or launch failed).
@@ -345,7 +354,9 @@ parallax_status_t parallax_prefill_train(const void* q, const void* rho, const v
 
 /* Bytes of workspace parallax_prefill_backward needs: dO split into bf16
  * high and low parts (2 x B H_q T d x 2 bytes) and two floats per row,
- * rounded to 16 bytes; 0 for non-positive sizes. */
+ * rounded to 16 bytes; 0 for a shape parallax_prefill_backward refuses
+ * (sizes <= 0, d not in {64, 128}, B or H_q above 65535, T + 256 of 2^22
+ * rows or more at d = 128, 2^23 at d = 64). */
 size_t parallax_prefill_backward_workspace_size(int B, int H_q, int T, int d);
 
 /* Gradients of the causal prefill output for an upstream gradient

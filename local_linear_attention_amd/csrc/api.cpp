@@ -51,8 +51,9 @@ parallax_status_t plan(int B, int H_q, int H_kv, int d, int S_max, int requested
   if (S_max > INT_MAX - kChunkQuantum) return PARALLAX_ERR_UNSUPPORTED;
   const int G = H_q / H_kv;
   const int hw = parallax::decode_heads_per_workgroup(G);
-  const long long groups = (G + hw - 1) / hw;
-  const long long streams = (long long)B * H_kv * groups;
+  const long long groups = ((long long)G + hw - 1) / hw;
+  // H_kv * groups <= H_q / hw + H_kv < 2^32, so this product stays below 2^63
+  const long long streams = (long long)B * ((long long)H_kv * groups);
   const int full = round_up(S_max, kChunkQuantum);
   int chunk;
   if (requested > 0) {
@@ -73,7 +74,10 @@ parallax_status_t plan(int B, int H_q, int H_kv, int d, int S_max, int requested
     // compute unit keep as many bytes in flight as one does at d = 128
     // (gqa shape at d = 64: 4 splits 17.2 us, 8 splits 16.5 us).
     const long long target = (long long)cus * (d <= 64 ? 2 : 1);
-    long long want = ((long long)S_max * streams + target - 1) / target;
+    // streams beyond 2048 target's worth give the 2048-key cap anyway; capping
+    // them keeps the product inside 64 bits
+    const long long st_c = streams < target * 2048 ? streams : target * 2048;
+    long long want = ((long long)S_max * st_c + target - 1) / target;
     if (want > 2048) want = 2048;  // the cap below, applied before the narrowing to int
     chunk = round_up(want, kChunkQuantum);
     if (chunk < kChunkQuantum) chunk = kChunkQuantum;
@@ -92,14 +96,27 @@ parallax_status_t plan(int B, int H_q, int H_kv, int d, int S_max, int requested
   return PARALLAX_OK;
 }
 
+// Workspaces of 2^62 bytes or more are refused (no device holds one): every
+// size below is then exact in size_t.
+constexpr unsigned long long kMaxWorkspace = 1ull << 62;
+
+// Whether the partial records and counters of a plan stay below kMaxWorkspace.
+bool workspace_fits(int B, int H_q, int d, int ns) {
+  const unsigned __int128 rec = (unsigned __int128)(unsigned)B * (unsigned)H_q * (unsigned)ns *
+                                (unsigned)(2 * d + 4) * sizeof(float);
+  const unsigned __int128 ctr = (unsigned __int128)(unsigned)B * (unsigned)H_q * sizeof(uint32_t) + 16;
+  return rec + ctr < kMaxWorkspace;
+}
+
 size_t records_bytes(int B, int H_q, int d, int ns) {
   return (size_t)B * H_q * ns * (size_t)(2 * d + 4) * sizeof(float);
 }
 
 // Partial records, then one 32-bit arrival counter per (b, query head) (an
 // upper bound on the (b, KV head, head group) streams), rounded to 16 bytes.
+// 0 for a one-split plan, a bad shape or a workspace past kMaxWorkspace.
 size_t workspace_bytes_for(int B, int H_q, int d, int ns) {
-  if (B <= 0 || H_q <= 0 || d <= 0 || ns <= 1) return 0;
+  if (B <= 0 || H_q <= 0 || d <= 0 || ns <= 1 || !workspace_fits(B, H_q, d, ns)) return 0;
   const size_t ctr = ((size_t)B * H_q * sizeof(uint32_t) + 15) / 16 * 16;
   return records_bytes(B, H_q, d, ns) + ctr;
 }
@@ -123,6 +140,8 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   const int G = H_q / H_kv;
   const long long esz = dtype == PARALLAX_F32 ? 4 : 2;
   if (((long long)S_max + 64) * d * esz >= (1LL << 31)) return PARALLAX_ERR_UNSUPPORTED;
+  // one sequence's queries under 2 GiB: keeps head counts and the grid well inside int
+  if ((long long)H_q * d * esz >= (1LL << 31)) return PARALLAX_ERR_UNSUPPORTED;
   if (B > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid y
   if (!std::isfinite(scale)) return PARALLAX_ERR_BAD_SHAPE;  // NaN or infinite scale
   if (!aligned16(q) || !aligned16(rho) || !aligned16(k) || !aligned16(v) ||
@@ -132,6 +151,7 @@ parallax_status_t check_decode(const void* q, const void* rho, const void* k, co
   parallax_status_t st = plan(B, H_q, H_kv, d, S_max, num_splits, &ns, &chunk);
   if (st != PARALLAX_OK) return st;
   if (ns > 65535) return PARALLAX_ERR_UNSUPPORTED;  // grid z
+  if (ns > 1 && !workspace_fits(B, H_q, d, ns)) return PARALLAX_ERR_UNSUPPORTED;
   const bool direct = (ns == 1);
   if ((direct || need_out) && !out) return PARALLAX_ERR_NULL_POINTER;
   if (out && !aligned16(out)) return PARALLAX_ERR_MISALIGNED;
@@ -255,6 +275,7 @@ parallax_status_t parallax_decode_combine(const int32_t* seq_lens, float* out, i
     parallax_status_t st = plan(B, H_q, H_kv, d, S_max, num_splits, &ns, &chunk);
     if (st != PARALLAX_OK) return st;
     if (ns == 1) return PARALLAX_OK;
+    if (!workspace_fits(B, H_q, d, ns)) return PARALLAX_ERR_UNSUPPORTED;
     const size_t need = workspace_bytes_for(B, H_q, d, ns);
     if (!workspace || workspace_bytes < need) return PARALLAX_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PARALLAX_ERR_MISALIGNED;
@@ -382,8 +403,12 @@ parallax_status_t parallax_prefill_chunked(const void* q, const void* rho, const
 
 namespace {
 
+// 0 for a shape the backward refuses (the bounds of check_prefill_shape, under
+// which every size here is exact).
 size_t bwd_workspace_bytes(int B, int H_q, int T, int d) {
-  if (B <= 0 || H_q <= 0 || T <= 0 || d <= 0) return 0;
+  if (B <= 0 || H_q <= 0 || T <= 0 || (d != 64 && d != 128) || B > 65535 || H_q > 65535 ||
+      ((long long)T + 256) * d * 4 >= (1LL << 31))
+    return 0;
   const size_t rows = (size_t)B * H_q * T;
   const size_t half = rows * d * 2;          // one bf16 copy of dO
   return ((2 * half + rows * 8) + 15) / 16 * 16;
