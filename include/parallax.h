@@ -97,8 +97,9 @@ const char* parallax_status_string(parallax_status_t s);
  * `num_splits` contiguous key ranges of `chunk` keys (a multiple of 128),
  * processed by separate workgroups whose partial softmax states are merged
  * by the combine step. `requested` = 0 picks a plan from the device's
- * compute-unit count and the head dim d (about one workgroup per compute
- * unit at d = 128, two at d = 64, whose rows are half as long); a positive
+ * compute-unit count (about one workgroup per compute unit; a workgroup
+ * has 8 waves for bf16 at d = 64, whose rows are half as long, else 4);
+ * a positive
  * value asks for that many splits (rounded so that chunk is a multiple of
  * 128). Writes the plan to *num_splits and *chunk (either may be NULL).
  * Returns PARALLAX_ERR_BAD_SHAPE for sizes <= 0 or H_q % H_kv != 0,

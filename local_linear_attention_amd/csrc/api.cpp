@@ -70,10 +70,10 @@ parallax_status_t plan(int B, int H_q, int H_kv, int d, int S_max, int requested
     // workgroup streams for so short a time that the merge's record reads
     // decide, while a few more splits still cut the latency of small batches
     // (one 1024-key sequence: 2 splits 11.0 us, 8 splits 7.5 us).
-    // At d = 64 a workgroup's rows are half as long, so two workgroups per
-    // compute unit keep as many bytes in flight as one does at d = 128
-    // (gqa shape at d = 64: 4 splits 17.2 us, 8 splits 16.5 us).
-    const long long target = (long long)cus * (d <= 64 ? 2 : 1);
+    // For bf16 at d = 64 the workgroup has 8 waves instead of 4 (its rows
+    // are half as long), and one per compute unit is again best (gqa shape
+    // at d = 64: 4 splits 15.7 us, 8 splits 16.4 us, 2 splits 16.8 us).
+    const long long target = (long long)cus;
     // streams beyond 2048 target's worth give the 2048-key cap anyway; capping
     // them keeps the product inside 64 bits
     const long long st_c = streams < target * 2048 ? streams : target * 2048;

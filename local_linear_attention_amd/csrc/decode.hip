@@ -22,9 +22,9 @@
 // reference (c) merge exactly: rescale by exp(m_j - M) and shift by
 // (c_j - c) as above, an associative and commutative merge.
 //
-// Work layout. A workgroup of 4 waves owns one (b, KV head, group of <= 4
-// query heads, or <= 8 when the KV head has more than 4, key range of
-// `chunk` keys). Each wave takes every 4th block
+// Work layout. A workgroup of 4 waves (8 for bf16 at d = 64) owns one (b,
+// KV head, group of <= 4 query heads, or <= 8 when the KV head has more
+// than 4, key range of `chunk` keys). Each wave takes every 4th (8th) block
 // of 32 keys. Per block a lane loads its K and V pieces from HBM into
 // registers with range-checked buffer loads (rows at or past the sequence
 // length come back as zeros, so padding is never read). Both are read in
@@ -62,8 +62,17 @@ namespace parallax {
 
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kBlockKeys = 32;
+
+// Waves per workgroup, by the bytes of one K or V row. With 128-byte rows
+// (bf16 at d = 64) eight waves keep as many bytes in flight per compute unit
+// as four do with 256-byte rows (bf16 at d = 128, fp32 at d = 64), with one
+// workgroup per compute unit (gqa shape at d = 64: 4 splits of 8 waves 15.7
+// us, against 16.0 for 8 splits of 4 waves, two workgroups per compute unit,
+// and 16.1 for 4 splits of 4 waves). With 256-byte rows eight waves measured
+// slower (4 heads per workgroup: 24.5 against 24.1 us; 8 heads: 25.65
+// against 25.52).
+constexpr int decode_waves(int row_bytes) { return row_bytes <= 128 ? 8 : 4; }
 constexpr float kRescaleLog2 = 8.0f;
 
 template <typename T, int D>
@@ -272,7 +281,7 @@ __device__ __forceinline__ typename Vec<V>::T merge_splits(const float* base,
 // t >= c). Without MT, seq_lens holds the key counts and every head sees
 // them all.
 template <typename T, int D, bool MT, int HG>
-__global__ __launch_bounds__(256) void decode_partial_kernel(
+__global__ __launch_bounds__(64 * decode_waves(D * sizeof(T))) void decode_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ rho, const T* __restrict__ kc,
     const T* __restrict__ vc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ past_lens, float* __restrict__ out, float* __restrict__ ws,
@@ -280,9 +289,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     int num_splits, float scale_log2) {
   using P = Dec<T, D>;
   constexpr int HW = 4 * HG;                         // query heads per workgroup
-  __shared__ __attribute__((aligned(16))) float lds_state[kWaves][HW][4];  // m, l, bs, cref per head
-  __shared__ __attribute__((aligned(16))) float lds_vec[kWaves][2][HW][D];  // A, C per head
-  __shared__ __attribute__((aligned(16))) char k_lds[kWaves][P::KLDS];  // bf16: each wave's K block
+  constexpr int NW = decode_waves(D * sizeof(T));    // waves per workgroup
+  constexpr int NT = 64 * NW;
+  __shared__ __attribute__((aligned(16))) float lds_state[NW][HW][4];  // m, l, bs, cref per head
+  __shared__ __attribute__((aligned(16))) float lds_vec[NW][2][HW][D];  // A, C per head
+  __shared__ __attribute__((aligned(16))) char k_lds[NW][P::KLDS];  // bf16: each wave's K block
 
   // Grid (KV head x head group, sequence, split): workgroups are dealt to
   // the 8 XCDs in linear order (x fastest), so every XCD gets the same
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const bool fused = counters != nullptr;            // last workgroup merges the splits
   if (j0 >= n && !direct) {                          // empty split: the merge skips it
     if (fused && n == 0 && split == 0) {             // no workgroup holds a key
-      for (int idx = threadIdx.x; idx < Gw * D; idx += 256)
+      for (int idx = threadIdx.x; idx < Gw * D; idx += NT)
         out[((size_t)b * H_q + h0) * D + idx] = 0.f;
     }
     return;
@@ -556,7 +567,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     }
   };
 
-  for (int blk = j0 + kBlockKeys * wave; blk < j1; blk += kBlockKeys * kWaves) {
+  for (int blk = j0 + kBlockKeys * wave; blk < j1; blk += kBlockKeys * NW) {
     Words<P::KW> kw[2][P::KSTEPS];
     Words<P::VW> vw[8];
     load_block(blk, kw, vw);
@@ -585,7 +596,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
   __syncthreads();
 
-  // ---- merge the 4 waves; finalise (one split) or write the partial record.
+  // ---- merge the waves; finalise (one split) or write the partial record.
   // The records of this workgroup's heads lie in one range of the workspace
   // (heads h0 .. h0 + Gw - 1, every split), reached through one descriptor.
   // With the fused merge they are written and read at the device-coherent
@@ -595,26 +606,26 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   float* const wbase = direct ? out : ws + ((size_t)b * H_q + h0) * num_splits * P::REC;
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc(wbase, direct ? 0u : (uint32_t)(Gw * num_splits * P::REC * 4));
-  // V dimensions per thread, as many as keep all 256 threads busy (1, 2 or
+  // V dimensions per thread, as many as keep the workgroup busy (1, 2 or
   // 4): wider LDS reads, record stores and record loads. Four only in the
   // 8-head instantiation (4 x 128 dims never reach 1024 items), so that the
   // 4-head kernel keeps its register count (164: three workgroups per
   // compute unit in long, ragged batches).
   const int V = (HG == 2 && Gw * D >= 1024) ? 4 : (Gw * D >= 512 ? 2 : 1);
   // Waves merge in LDS. Branch-free: every LDS read of an item is issued
-  // before any is used (the states of the 4 waves as one 16-byte read each),
+  // before any is used (the state of each wave as one 16-byte read),
   // waves without keys (l = 0) get weight 0, and the reference c0 is the
   // first wave's with keys.
   auto wave_merge = [&](auto vtag) {
     constexpr int VV = decltype(vtag)::value;
     using VT = typename Vec<VV>::T;
-    for (int idx = tid; idx < Gw * D / VV; idx += 256) {
+    for (int idx = tid; idx < Gw * D / VV; idx += NT) {
       const int h = idx / (D / VV);
       const int q = idx % (D / VV);
-      float4 st[kWaves];  // m, l, bs, cref
-      VT Aw[kWaves], Cw[kWaves];
+      float4 st[NW];  // m, l, bs, cref
+      VT Aw[NW], Cw[NW];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         st[w] = *reinterpret_cast<const float4*>(&lds_state[w][h][0]);
         Aw[w] = *reinterpret_cast<const VT*>(&lds_vec[w][0][h][VV * q]);
         Cw[w] = *reinterpret_cast<const VT*>(&lds_vec[w][1][h][VV * q]);
@@ -622,14 +633,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       float M = -INFINITY;
       float c0 = 0.f;
 #pragma unroll
-      for (int w = kWaves - 1; w >= 0; --w) {
+      for (int w = NW - 1; w >= 0; --w) {
         M = st[w].y > 0.f ? fmaxf(M, st[w].x) : M;
         c0 = st[w].y > 0.f ? st[w].w : c0;
       }
       float l = 0.f, bs = 0.f;
       VT A{}, C{};
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float lw = st[w].y;
         const float al = lw > 0.f ? exp2f(st[w].x - M) : 0.f;
         const float sh = st[w].w - c0;
@@ -685,7 +696,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   auto split_merge = [&](auto vtag) {
     constexpr int VV = decltype(vtag)::value;
     using VT = typename Vec<VV>::T;
-    for (int idx = tid; idx < Gw * D / VV; idx += 256) {  // (head, VV dims)
+    for (int idx = tid; idx < Gw * D / VV; idx += NT) {  // (head, VV dims)
       const int h = idx / (D / VV);
       const int q = idx % (D / VV);
       *reinterpret_cast<VT*>(out + ((size_t)b * H_q + h0 + h) * D + VV * q) =
@@ -720,7 +731,7 @@ template <typename T, int D, bool MT, int HG>
 hipError_t launch_partial_hg(const DecodeArgs& a, hipStream_t st) {
   const int ngroups = (a.G + 4 * HG - 1) / (4 * HG);
   dim3 grid(a.H_kv * ngroups, a.B, a.num_splits);  // stream fastest in the linear order
-  hipLaunchKernelGGL((decode_partial_kernel<T, D, MT, HG>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((decode_partial_kernel<T, D, MT, HG>), grid, dim3(64 * decode_waves(D * sizeof(T))), 0, st,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.rho),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.seq_lens,
                      a.past_lens, a.out, static_cast<float*>(a.ws),
