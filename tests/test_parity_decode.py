@@ -265,6 +265,16 @@ def test_gqa8_full_size_sampled():
     _sampled(w, heads)
 
 
+def test_gqa_d64_full_size_sampled():
+    """The gqa-decode shape at head dim 64 (8 x 4096 keys, 16 query heads on 8
+    KV heads) in the automatic plan the benchmark times (4 splits of 1024
+    keys, 8-wave workgroups): every head of the first and last sequence."""
+    w = replace_shape(WORKLOADS[2], name="gqa-decode-d64", d=64, q_std=64 ** -0.25,
+                      k_std=64 ** -0.25)
+    heads = [(0, h) for h in range(16)] + [(7, h) for h in range(16)]
+    _sampled(w, heads)
+
+
 @pytest.mark.slow
 def test_workload3_full_sampled():
     w = WORKLOADS[3]
@@ -298,16 +308,18 @@ def test_fused_workspace_reuse_counters_return_to_zero():
 
 
 @pytest.mark.slow
-def test_longest_cache_accepted():
+@pytest.mark.parametrize("d", [128, 64])
+def test_longest_cache_accepted(d):
     """The longest KV cache the ABI accepts, (S_max + 64) d * 2 bytes just under 2^31
-    per (b, KV head) for bf16, d = 128: the last rows' byte offsets sit next to 2^31.
-    The sequence ends 5 keys before S_max (NaN padding after it). Automatic plan,
-    and one workgroup per head group streaming all of it."""
-    d = 128
+    per (b, KV head) for bf16 (d = 128 and d = 64, whose workgroups have 8 waves):
+    the last rows' byte offsets sit next to 2^31. The sequence ends 5 keys before
+    S_max (NaN padding after it). Automatic plan, and one workgroup per head group
+    streaming all of it."""
     S = (1 << 31) // (d * 2) - 64 - 1
     n = S - 5
-    w = replace_shape(WORKLOADS[2], B=1, H_q=2, H_kv=1, S_max=S)
-    print(f"[decode parity] longest cache S_max={S} n={n}", flush=True)
+    w = replace_shape(WORKLOADS[2], B=1, H_q=2, H_kv=1, d=d, S_max=S, q_std=d ** -0.25,
+                      k_std=d ** -0.25)
+    print(f"[decode parity] longest cache d={d} S_max={S} n={n}", flush=True)
     dev = make_decode_inputs(w, device="cuda", seq_lens=[n])
     outs = {ns: run_decode(dev, ns) for ns in (0, 1)}
     K = oracle.parallax_oracle._f64(dev["k_cache"][0, 0, :n].cpu())
